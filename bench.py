@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark: restore losslessly coded BF16 weights on one MI355X.
+
+One step = one pass of the whole restore over one batch of synthetic coded
+weights already resident in HBM: the workload's tensors are decoded by one
+afx_decode_layer_async call (one kernel launch for up to 32 tensors).
+
+Default workload: one Qwen3-14B-shaped decoder layer (11 tensors, 330.3M
+BF16 values, 0.66 GB restored), the unit the time-to-ready model of "Why
+Weight Offloading Slows Inference" reasons about. Other workloads:
+tensor-1024 (1024x1024), q_proj (5120x5120), embedding (151936x5120).
+
+Prints one JSON line with the throughput of restored BF16, the HBM roofline
+fraction of the decode kernel (hipEvent timing on the launch stream), and the
+CPU oracle's decode rate on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decoded BF16 GB/s on 1 MI355X + % of HBM roofline; bit-exact vs CPU oracle"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_weight_afx_amd", "csrc", "afx_decode.hip")
+KERNEL_NAME = "afx_decode_kernel"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def host_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def workload_specs(name: str):
+    from lossless_bf16_weight_afx_amd import synth
+
+    if name == "layer":
+        return "qwen3-14b-decoder-layer", synth.decoder_layer(0)
+    if name == "tensor-1024":
+        return "bf16-1024x1024", synth.single_tensor(1024, 1024, 1)
+    if name == "q_proj":
+        return "qwen3-14b-q_proj-5120x5120", synth.single_tensor(5120, 5120, 2)
+    if name == "embedding":
+        return "qwen3-14b-embedding-151936x5120", synth.embedding()
+    raise SystemExit(f"unknown workload {name}")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profile_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = (t.strip() for t in line.split("=", 1))
+            kv[k] = v
+    if kv.get("kernel_sha") != kernel_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer", choices=["layer", "tensor-1024", "q_proj", "embedding"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotate over this many blob/output copies (default: enough for >1 GB per pass)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the restore is per-tensor work with no collective; "
+              "run it with --gpus 1 (see DESIGN.md for how it would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from lossless_bf16_weight_afx_amd import afx, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    afx.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    threads = min(16, host_threads())
+    workload, specs = workload_specs(args.workload)
+
+    # ---- inputs: generate, encode with the library's encoder, move to HBM
+    t0 = time.time()
+    xs, blobs, infos = [], [], []
+    for sp in specs:
+        x = synth.generate(sp, threads=threads)
+        blob = afx.afx_encode(x, sp.shape, threads=threads)
+        xs.append(x)
+        blobs.append(blob)
+        infos.append(afx.afx_query(blob))
+    n_total = sum(int(i.n_elems) for i in infos)
+    blob_total = sum(int(i.blob_bytes) for i in infos)
+    restored = 2 * n_total
+    log(f"[bench] {workload}: {len(specs)} tensors, {n_total} values, blob {blob_total} B "
+        f"(ratio {blob_total / restored:.4f}); inputs ready in {time.time() - t0:.1f}s")
+
+    traffic_pass = blob_total + restored
+    copies = args.copies or max(1, int(np.ceil(1.0e9 / traffic_pass)))
+    copies = min(copies, 64)
+    dblobs = [[torch.from_numpy(b).to(dev) for b in blobs] for _ in range(copies)]
+    douts = [[torch.empty(int(i.n_elems), dtype=torch.int16, device=dev) for i in infos] for _ in range(copies)]
+    jobsets = [afx.make_jobs([(i, b.data_ptr(), o.data_ptr(), 2 * int(i.n_elems))
+                              for i, b, o in zip(infos, dblobs[c], douts[c])]) for c in range(copies)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    # ---- correctness pass (separate from timing): every copy, bit-exact
+    for c in range(copies):
+        afx.afx_decode_layer_async(jobsets[c], sp)
+    torch.cuda.synchronize()
+    exact = True
+    for t, x in enumerate(xs):
+        ref = torch.from_numpy(x.view(np.int16)).to(dev)
+        for c in range(copies):
+            exact &= bool(torch.equal(ref, douts[c][t]))
+        del ref
+    if not exact:
+        log("[bench] restored bits differ from the originals")
+
+    # ---- timing: hipEvents on the launch stream around every launch
+    for w in range(args.warmup):
+        afx.afx_decode_layer_async(jobsets[w % copies], sp)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for k in range(args.steps):
+        starts[k].record(stream)
+        afx.afx_decode_layer_async(jobsets[k % copies], sp)
+        ends[k].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    launch_ms = float(np.mean(per_launch_ms))
+    value = restored / (ms_per_step * 1e-3) / 1e9
+
+    # ---- plain device copy of the same bytes: the box's practical ceiling
+    src = torch.empty(traffic_pass // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    achieved = traffic_pass / (launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(args.workload),
+                "algorithmic_bytes_per_launch": traffic_pass, "kernel": KERNEL_NAME,
+                "kernel_ms": round(launch_ms, 5), "copy_ceiling_GBps": round(copy_gbps, 1)}
+
+    # ---- CPU oracle baseline on this host, and bit-exactness against it
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        sample_tensors = list(range(len(specs)))
+        t0 = time.perf_counter()
+        dec = [oracle.decode(blobs[i], threads=threads) for i in sample_tensors]
+        t_cpu = time.perf_counter() - t0
+        n_cpu = sum(d.size for d in dec)
+        for i, d in zip(sample_tensors, dec):
+            exact &= bool(np.array_equal(d, douts[0][i].cpu().numpy().view(np.uint16)))
+        cpu = {"value": round(2 * n_cpu / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"whole {workload} ({n_cpu} values), bit-serial canonical decode, chunk-parallel "
+                         f"over {threads} threads, one pass", "seconds": round(t_cpu, 2)}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": workload, "tensors": len(specs), "values": n_total, "restored_bytes": restored,
+                   "blob_bytes": blob_total, "ratio": round(blob_total / restored, 4), "copies": copies,
+                   "encoder": "libafx afx_encode"},
+        "bit_exact": bool(exact), "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if exact else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

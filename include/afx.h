@@ -1,0 +1,149 @@
+/*
+ * afx.h -- C ABI of libafx: lossless BF16 weight blobs restored on the GPU.
+ *
+ * The operation. "Why Weight Offloading Slows Inference" (section "Three
+ * steps for each weight", Eq. (1)) puts an unpack step, t_unpack, between
+ * reading a stored weight and using it; section "Lossless compression" stores
+ * BF16 weights with shorter codes for common exponent values (Huffman's
+ * minimum-redundancy code, that page's reference [2]) and restores the exact
+ * released bits before compute. This library performs that restore on an
+ * AMD Instinct MI355X (gfx950), after the compressed bytes have been copied
+ * to device memory, and writes the BF16 bit patterns into a caller buffer.
+ *
+ * Blob format (version 1), little-endian; every section starts on a
+ * 256-byte boundary and the blob length is a multiple of 256:
+ *   [0,256)        header: "AFX1", u32 version = 1, u64 n, u64 total_bits,
+ *                  u64 exp_words, u32 ndim, u32 4096, u32 32, u32 12,
+ *                  u32 n_symbols, 12 zero bytes, u64 shape[4] at byte 64, zeros
+ *   code_len[256]  u8 code length of each exponent value (0 = unused, <= 12)
+ *   chunk_base     u64 x (n_chunks + 1): bit position where each 4096-element
+ *                  chunk starts; the last entry equals total_bits
+ *   gap            u16 x n_groups: start of each 32-element group, in bits
+ *                  after its chunk's base
+ *   signmant       u8 x n: (sign << 7) | mantissa7 of each element
+ *   exp            u32 x exp_words: the canonical code stream of the 8-bit
+ *                  exponent fields, MSB first in each word, then zero words
+ * Element i is ((signmant[i] & 0x80) << 8) | (exponent << 7) |
+ * (signmant[i] & 0x7F). The code is canonical: symbols ordered by (length,
+ * value) take consecutive codes; a tensor with one exponent value uses one
+ * 1-bit code.
+ *
+ * Conventions. Every function returns AFX_OK (0) or a negative afx_status,
+ * never aborts and never prints. Argument and format errors are detected
+ * before any HIP call and leave every output untouched. The library keeps no
+ * pointer after a call returns and allocates no device memory.
+ */
+#ifndef AFX_H
+#define AFX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AFX_ABI_VERSION 1u
+#define AFX_FORMAT_VERSION 1u
+#define AFX_CHUNK_ELEMS 4096u
+#define AFX_GROUP_ELEMS 32u
+#define AFX_MAX_CODE_LEN 12u
+#define AFX_MAX_JOBS_PER_LAUNCH 32u
+
+typedef enum afx_status {
+    AFX_OK = 0,
+    AFX_E_INVALID_ARG = -1,     /* NULL pointer, zero-size or inconsistent argument */
+    AFX_E_BAD_MAGIC = -2,       /* blob does not start with "AFX1" */
+    AFX_E_BAD_VERSION = -3,     /* unknown format version or fixed-field value */
+    AFX_E_CORRUPT = -4,         /* inconsistent header, code lengths, bases or gaps */
+    AFX_E_BUFFER_TOO_SMALL = -5,/* blob shorter than its header says, or output too small */
+    AFX_E_MISALIGNED = -6,      /* device pointer not 16-byte aligned */
+    AFX_E_HIP = -7,             /* a HIP runtime call failed (launch or execution) */
+    AFX_E_UNSUPPORTED = -8      /* request beyond what this build supports */
+} afx_status;
+
+/* What afx_query reports about a blob. Offsets are in bytes from the blob's
+ * first byte; sizes count elements unless named *_bytes. */
+typedef struct afx_info {
+    uint32_t abi_version;     /* AFX_ABI_VERSION of the library that filled it */
+    uint32_t format_version;  /* 1 */
+    uint64_t n_elems;         /* BF16 elements restored */
+    uint64_t decoded_bytes;   /* 2 * n_elems */
+    uint64_t blob_bytes;      /* bytes of the blob, a multiple of 256 */
+    uint64_t total_bits;      /* length of the exponent code stream */
+    uint64_t exp_words;       /* u32 words of the exp section, padding included */
+    uint64_t n_chunks;        /* ceil(n / 4096) */
+    uint64_t n_groups;        /* ceil(n / 32) */
+    uint32_t ndim;            /* 0..4 */
+    uint32_t n_symbols;       /* exponent values in use */
+    uint64_t shape[4];        /* unused dimensions are 0 */
+    uint32_t chunk_elems;     /* 4096 */
+    uint32_t group_elems;     /* 32 */
+    uint32_t max_code_len;    /* 12 */
+    uint32_t longest_code;    /* longest length actually used */
+    uint64_t off_code_len, off_chunk_base, off_gap, off_signmant, off_exp;
+} afx_info;
+
+/* One tensor of a batch. */
+typedef struct afx_job {
+    const afx_info *info;  /* filled by afx_query from a host copy of the blob */
+    const void *blob_dev;  /* device copy of the same blob, 16-byte aligned */
+    void *out_dev;         /* device output of n_elems u16 (BF16), 16-byte aligned */
+    size_t out_bytes;      /* capacity of out_dev in bytes, >= 2 * n_elems */
+} afx_job;
+
+/* afx_query: inspect a blob held in host memory (pageable or pinned).
+ * Checks the header, the code lengths (each <= 12; Kraft sum exactly 1 when
+ * two or more values are used, a single 1-bit code otherwise), the chunk
+ * bases (start at 0, non-decreasing, at most 12 bits per element, end at
+ * total_bits) and the group gaps (0 at each chunk start, non-decreasing,
+ * within the chunk), then fills *info. Host only, no HIP call.
+ * Errors: AFX_E_INVALID_ARG (NULL), AFX_E_BUFFER_TOO_SMALL (blob_bytes short),
+ * AFX_E_BAD_MAGIC, AFX_E_BAD_VERSION, AFX_E_CORRUPT. */
+int afx_query(const void *blob_host, size_t blob_bytes, afx_info *info);
+
+/* afx_decode_tensor: restore one tensor and wait for it.
+ * info comes from afx_query on a host copy of the blob whose device copy is
+ * blob_dev. Writes exactly 2 * n_elems bytes at out_dev and nothing else.
+ * stream is a hipStream_t (NULL = the default stream); the call enqueues the
+ * decode on it and then synchronizes that stream, so asynchronous kernel
+ * errors are reported too. Output must not overlap the blob.
+ * Errors: AFX_E_INVALID_ARG, AFX_E_BUFFER_TOO_SMALL (out_bytes < 2n),
+ * AFX_E_MISALIGNED, AFX_E_HIP. A device blob that differs from the validated
+ * host copy decodes to wrong values but never reads or writes out of bounds. */
+int afx_decode_tensor(const afx_info *info, const void *blob_dev, void *out_dev, size_t out_bytes,
+                      void *stream);
+
+/* afx_decode_layer_async: restore a batch of tensors (e.g. the 11 tensors of
+ * one decoder layer, the unit that page's section "Loading during
+ * computation" prefetches) with one launch per AFX_MAX_JOBS_PER_LAUNCH jobs,
+ * enqueued on stream; returns without waiting. Completion is observed through
+ * the stream or events recorded on it. All jobs are checked before anything
+ * is enqueued. Errors: as afx_decode_tensor, but only enqueue-time HIP errors
+ * are reported. */
+int afx_decode_layer_async(const afx_job *jobs, size_t n_jobs, void *stream);
+
+/* afx_status_str: a static description of a status code. */
+const char *afx_status_str(int status);
+
+/* ---- Encoder (host). Produces format-1 blobs; the code lengths are an
+ * optimal prefix code limited to 12 bits over the tensor's exponent values. */
+
+/* afx_encode_plan: histogram the exponents of x (n BF16 bit patterns), pick
+ * the code lengths, and report the stream length and the blob size.
+ * threads <= 0 picks the hardware thread count. */
+int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len[256],
+                    uint64_t *total_bits, uint64_t *blob_bytes);
+
+/* afx_encode: write the blob for x with the lengths and stream length from
+ * afx_encode_plan into blob (host memory, blob_bytes >= the planned size).
+ * shape has ndim entries (ndim 1..4, product == n). */
+int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape,
+               const uint8_t code_len[256], uint64_t total_bits, void *blob, size_t blob_bytes,
+               int threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AFX_H */

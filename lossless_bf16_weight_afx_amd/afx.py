@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libafx (``include/afx.h``), same names as the C ABI.
+
+Argument marshalling only: every step of the restore runs in the library's
+HIP kernels. PyTorch supplies device buffers and streams. If ``libafx.so`` has
+not been built, loading raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libafx.so")
+
+AFX_OK = 0
+AFX_E_INVALID_ARG = -1
+AFX_E_BAD_MAGIC = -2
+AFX_E_BAD_VERSION = -3
+AFX_E_CORRUPT = -4
+AFX_E_BUFFER_TOO_SMALL = -5
+AFX_E_MISALIGNED = -6
+AFX_E_HIP = -7
+AFX_E_UNSUPPORTED = -8
+MAX_JOBS_PER_LAUNCH = 32
+
+# Every symbol include/afx.h declares.
+EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_status_str",
+           "afx_encode_plan", "afx_encode")
+
+
+class AfxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+class afx_info(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32),
+        ("format_version", ctypes.c_uint32),
+        ("n_elems", ctypes.c_uint64),
+        ("decoded_bytes", ctypes.c_uint64),
+        ("blob_bytes", ctypes.c_uint64),
+        ("total_bits", ctypes.c_uint64),
+        ("exp_words", ctypes.c_uint64),
+        ("n_chunks", ctypes.c_uint64),
+        ("n_groups", ctypes.c_uint64),
+        ("ndim", ctypes.c_uint32),
+        ("n_symbols", ctypes.c_uint32),
+        ("shape", ctypes.c_uint64 * 4),
+        ("chunk_elems", ctypes.c_uint32),
+        ("group_elems", ctypes.c_uint32),
+        ("max_code_len", ctypes.c_uint32),
+        ("longest_code", ctypes.c_uint32),
+        ("off_code_len", ctypes.c_uint64),
+        ("off_chunk_base", ctypes.c_uint64),
+        ("off_gap", ctypes.c_uint64),
+        ("off_signmant", ctypes.c_uint64),
+        ("off_exp", ctypes.c_uint64),
+    ]
+
+
+class afx_job(ctypes.Structure):
+    _fields_ = [
+        ("info", ctypes.POINTER(afx_info)),
+        ("blob_dev", ctypes.c_void_p),
+        ("out_dev", ctypes.c_void_p),
+        ("out_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libafx.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise OSError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or python -m lossless_bf16_weight_afx_amd.build")
+        L = ctypes.CDLL(_LIB_PATH)
+        u8p, u16p, u64p = (ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_uint16),
+                           ctypes.POINTER(ctypes.c_uint64))
+        L.afx_query.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(afx_info)]
+        L.afx_query.restype = ctypes.c_int
+        L.afx_decode_tensor.argtypes = [ctypes.POINTER(afx_info), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.afx_decode_tensor.restype = ctypes.c_int
+        L.afx_decode_layer_async.argtypes = [ctypes.POINTER(afx_job), ctypes.c_size_t, ctypes.c_void_p]
+        L.afx_decode_layer_async.restype = ctypes.c_int
+        L.afx_status_str.argtypes = [ctypes.c_int]
+        L.afx_status_str.restype = ctypes.c_char_p
+        L.afx_encode_plan.argtypes = [u16p, ctypes.c_uint64, ctypes.c_int, u8p, u64p, u64p]
+        L.afx_encode_plan.restype = ctypes.c_int
+        L.afx_encode.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint32, u64p, u8p, ctypes.c_uint64,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        L.afx_encode.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().afx_status_str(status).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != AFX_OK:
+        raise AfxError(rc, what)
+
+
+# ---------------------------------------------------------------------------
+# C entry points
+# ---------------------------------------------------------------------------
+def afx_query(blob_host, blob_bytes: int | None = None) -> afx_info:
+    """Validate a host blob (numpy uint8 array, or an address with a size)."""
+    info = afx_info()
+    if isinstance(blob_host, np.ndarray):
+        assert blob_host.dtype == np.uint8 and blob_host.flags.c_contiguous
+        ptr, size = blob_host.ctypes.data, blob_host.size if blob_bytes is None else blob_bytes
+    else:
+        ptr, size = int(blob_host), int(blob_bytes)
+    _check(lib().afx_query(ctypes.c_void_p(ptr), size, ctypes.byref(info)), "afx_query")
+    return info
+
+
+def afx_decode_tensor(info: afx_info, blob_dev: int, out_dev: int, out_bytes: int, stream: int = 0) -> None:
+    """Restore one tensor; blocks until the stream has finished it."""
+    _check(lib().afx_decode_tensor(ctypes.byref(info), ctypes.c_void_p(blob_dev), ctypes.c_void_p(out_dev),
+                                   out_bytes, ctypes.c_void_p(stream)), "afx_decode_tensor")
+
+
+def make_jobs(jobs) -> ctypes.Array:
+    """Pack (info, blob_dev, out_dev, out_bytes) tuples into an afx_job array.
+
+    The returned array refers to the afx_info objects; keep them alive.
+    """
+    arr = (afx_job * len(jobs))()
+    for i, (info, blob_dev, out_dev, out_bytes) in enumerate(jobs):
+        arr[i].info = ctypes.pointer(info)
+        arr[i].blob_dev = blob_dev
+        arr[i].out_dev = out_dev
+        arr[i].out_bytes = out_bytes
+    return arr
+
+
+def afx_decode_layer_async(jobs, stream: int = 0) -> None:
+    """Enqueue the restore of a batch of tensors on `stream`; returns at once.
+
+    ``jobs`` is an afx_job array from make_jobs, or a list of tuples.
+    """
+    arr = jobs if isinstance(jobs, ctypes.Array) else make_jobs(jobs)
+    _check(lib().afx_decode_layer_async(arr, len(arr), ctypes.c_void_p(stream)), "afx_decode_layer_async")
+
+
+def afx_encode_plan(x: np.ndarray, threads: int = 0):
+    """Code lengths (256 u8), stream bits and blob size for BF16 bits x."""
+    x = np.ascontiguousarray(x, dtype=np.uint16).ravel()
+    lens = np.zeros(256, np.uint8)
+    bits = ctypes.c_uint64()
+    nbytes = ctypes.c_uint64()
+    _check(lib().afx_encode_plan(x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), x.size, threads,
+                                 lens.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), ctypes.byref(bits),
+                                 ctypes.byref(nbytes)), "afx_encode_plan")
+    return lens, bits.value, nbytes.value
+
+
+def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None) -> np.ndarray:
+    """Encode BF16 bits x into a blob.
+
+    ``out`` may be a numpy uint8 array or a host address (int) with room for
+    the planned size (e.g. pinned memory); the blob bytes are returned as a
+    numpy view when out is an array or None, else the size is returned.
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    if shape is None:
+        shape = x.shape if x.ndim else (1,)
+    x = x.ravel()
+    lens, bits, nbytes = afx_encode_plan(x, threads)
+    shp = (ctypes.c_uint64 * 4)(*(list(shape) + [0] * (4 - len(shape))))
+    if out is None:
+        out = np.empty(nbytes, np.uint8)
+    if isinstance(out, np.ndarray):
+        assert out.dtype == np.uint8 and out.size >= nbytes
+        addr, cap = out.ctypes.data, out.size
+    else:
+        addr, cap = int(out[0]), int(out[1])
+    _check(lib().afx_encode(x.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), x.size, len(shape), shp,
+                            lens.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), bits, ctypes.c_void_p(addr),
+                            cap, threads), "afx_encode")
+    return out[:nbytes] if isinstance(out, np.ndarray) else nbytes
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences (buffers and streams only)
+# ---------------------------------------------------------------------------
+def to_device(blob: np.ndarray, device="cuda"):
+    """Copy a host blob into a fresh uint8 device tensor (256-byte aligned)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(blob)).to(device)
+
+
+def decode(info: afx_info, blob_dev, out=None, stream=None):
+    """Restore into a torch int16 device tensor (bit patterns of BF16)."""
+    import torch
+
+    if out is None:
+        out = torch.empty(int(info.n_elems), dtype=torch.int16, device=blob_dev.device)
+    s = stream if stream is not None else torch.cuda.current_stream(blob_dev.device)
+    afx_decode_tensor(info, blob_dev.data_ptr(), out.data_ptr(), out.numel() * out.element_size(), s.cuda_stream)
+    return out

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP restore against the original bits and the CPU oracle.
+
+Blobs come from the oracle's encoder; the expected values are the generated
+inputs themselves, which the oracle decoder reproduces bit for bit (pinned in
+test_oracle_pins.py). Every comparison is exact (integer bit patterns).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_bf16_weight_afx_amd import afx, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    afx.lib()
+    return torch.device("cuda:0")
+
+
+def restore(blob: np.ndarray, guard: int = 64):
+    """Decode on the GPU into a buffer with sentinel words after the output."""
+    info = afx.afx_query(blob)
+    dev = afx.to_device(blob)
+    n = int(info.n_elems)
+    out = torch.full((n + guard,), 0x5A5A, dtype=torch.int16, device="cuda")
+    afx.afx_decode_tensor(info, dev.data_ptr(), out.data_ptr(), 2 * n, torch.cuda.current_stream().cuda_stream)
+    tail = out[n:].cpu().numpy()
+    assert np.all(tail == 0x5A5A), "wrote past the output"
+    return out[:n].cpu().numpy().view(np.uint16)
+
+
+def check(x: np.ndarray, name: str):
+    say(f"[gpu] case {name}: n={x.size}")
+    blob = oracle.encode(x)
+    y = restore(blob)
+    x = x.ravel()
+    if not np.array_equal(y, x):
+        bad = np.nonzero(y != x)[0]
+        raise AssertionError(f"{name}: {bad.size} mismatches, first at {bad[:5]}: got {y[bad[:5]]} want {x[bad[:5]]}")
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 128, 4095, 4096, 4097, 5120, 3 * 4096 + 17, 64 * 4096 + 4000])
+def test_sizes(n):
+    rng = np.random.default_rng(n)
+    x = synth.f32_to_bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    check(x, f"normal-n{n}")
+
+
+def test_empty_tensor():
+    blob = oracle.encode(np.zeros(0, np.uint16))
+    info = afx.afx_query(blob)
+    dev = afx.to_device(blob)
+    afx.afx_decode_tensor(info, dev.data_ptr(), 0, 0, torch.cuda.current_stream().cuda_stream)
+
+
+def test_special_patterns():
+    check(np.arange(65536, dtype=np.uint16), "all-65536-patterns")
+    check(np.zeros(10000, np.uint16), "all-zero")
+    check(np.full(4097, 0x3F80, np.uint16), "constant")
+    specials = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x0001, 0x807F, 0x7F7F], np.uint16)
+    x = np.tile(specials, 5000)
+    np.random.default_rng(1).shuffle(x)
+    check(x, "nan-inf-zero-subnormal")
+
+
+def test_longest_codes():
+    # a Fibonacci histogram forces many 12-bit codes
+    fib = [1, 1]
+    while len(fib) < 30:
+        fib.append(fib[-1] + fib[-2])
+    counts = np.array(fib) * 3
+    x = np.repeat((np.arange(30, dtype=np.uint16) + 100) << 7, counts)
+    np.random.default_rng(2).shuffle(x)
+    x = x[:200_000] | np.uint16(0x8055)
+    blob = oracle.encode(x)
+    assert oracle.sections(blob)["code_len"].max() == 12
+    check(x, "fibonacci-12-bit-codes")
+
+
+def test_c1_tensor():
+    check(synth.generate(synth.single_tensor()[0]), "1024x1024")
+
+
+def test_c2_q_proj():
+    check(synth.generate(synth.single_tensor(5120, 5120, 2)[0]), "5120x5120")
+
+
+def test_heavy_tail_slice():
+    spec = synth.TensorSpec("t4", (4096, 5120), "t4", 4)
+    check(synth.generate(spec), "t4-4096x5120")
+
+
+def test_matches_oracle_decoder():
+    x = synth.generate(synth.TensorSpec("t", (300, 4096), "t4", 8))
+    blob = oracle.encode(x)
+    assert np.array_equal(restore(blob), oracle.decode(blob, threads=4))
+
+
+def test_library_encoder_blob():
+    x = synth.generate(synth.TensorSpec("t", (777, 5120), "normal", 9))
+    blob = afx.afx_encode(x, (777, 5120))
+    say("[gpu] case library-encoder blob")
+    assert np.array_equal(restore(blob), x)
+
+
+def test_misaligned_output_rejected():
+    x = synth.generate(synth.TensorSpec("t", (4096,), "normal", 3))
+    blob = oracle.encode(x)
+    info = afx.afx_query(blob)
+    dev = afx.to_device(blob)
+    out = torch.full((4096 + 8,), 7, dtype=torch.int16, device="cuda")
+    with pytest.raises(afx.AfxError) as e:
+        afx.afx_decode_tensor(info, dev.data_ptr(), out.data_ptr() + 2, 8192, 0)
+    assert e.value.status == afx.AFX_E_MISALIGNED
+    assert torch.all(out == 7).item()
+
+
+def layer_blobs(layer=0):
+    specs = synth.decoder_layer(layer)
+    xs, blobs = [], []
+    for sp in specs:
+        say(f"[gpu] encode {sp.name} {sp.shape}")
+        x = synth.generate(sp)
+        xs.append(x)
+        blobs.append(oracle.encode(x, sp.shape))
+    return specs, xs, blobs
+
+
+def test_layer_batch_one_launch():
+    """The 11 tensors of a Qwen3-14B-shaped layer restored by one enqueue."""
+    specs, xs, blobs = layer_blobs(0)
+    infos = [afx.afx_query(b) for b in blobs]
+    devs = [afx.to_device(b) for b in blobs]
+    outs = [torch.empty(x.size + 64, dtype=torch.int16, device="cuda").fill_(0x5A5A) for x in xs]
+    jobs = afx.make_jobs([(i, d.data_ptr(), o.data_ptr(), 2 * x.size) for i, d, o, x in zip(infos, devs, outs, xs)])
+    say("[gpu] case layer batch (11 tensors, one launch)")
+    afx.afx_decode_layer_async(jobs, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for sp, x, o in zip(specs, xs, outs):
+        y = o.cpu().numpy().view(np.uint16)
+        assert np.all(y[x.size:] == 0x5A5A), sp.name
+        assert np.array_equal(y[:x.size], x), sp.name
+    # the same tensors one by one give the same bits
+    for sp, x, i, d in zip(specs, xs, infos, devs):
+        o = torch.empty(x.size, dtype=torch.int16, device="cuda")
+        afx.afx_decode_tensor(i, d.data_ptr(), o.data_ptr(), 2 * x.size, 0)
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), x), sp.name
+
+
+def test_many_small_tensors_split_over_launches():
+    """More jobs than one launch holds: 40 tensors of mixed sizes."""
+    rng = np.random.default_rng(4)
+    xs = [synth.generate(synth.TensorSpec(f"t{i}", (int(rng.integers(1, 30000)),), "normal", 500 + i))
+          for i in range(40)]
+    blobs = [oracle.encode(x) for x in xs]
+    infos = [afx.afx_query(b) for b in blobs]
+    devs = [afx.to_device(b) for b in blobs]
+    outs = [torch.empty(x.size, dtype=torch.int16, device="cuda") for x in xs]
+    say("[gpu] case 40 small tensors")
+    afx.afx_decode_layer_async([(i, d.data_ptr(), o.data_ptr(), 2 * x.size)
+                                for i, d, o, x in zip(infos, devs, outs, xs)], 0)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, outs):
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
+
+
+def test_embedding_full_size():
+    """151936 x 5120 heavy-tailed tensor, bit-exact in full."""
+    spec = synth.embedding()[0]
+    say("[gpu] generate embedding")
+    x = synth.generate(spec)
+    say("[gpu] oracle-encode embedding")
+    blob = oracle.encode(x, spec.shape)
+    info = afx.afx_query(blob)
+    dev = afx.to_device(blob)
+    del blob
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    out = torch.empty_like(xd)
+    say("[gpu] case embedding 151936x5120")
+    afx.afx_decode_tensor(info, dev.data_ptr(), out.data_ptr(), 2 * x.size, torch.cuda.current_stream().cuda_stream)
+    assert torch.equal(out, xd)
