@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerEU = 4;  // occupancy target: LDS allows 4 blocks of 4 waves per CU
 constexpr int kThreads = kWave * kWavesPerBlock;
 constexpr int kLutEntries = 1 << kMaxLen;  // 4096
 
@@ -46,6 +47,7 @@ struct TensorDesc {
     uint16_t *out;
     uint64_t n;
     uint64_t exp_words;
+    uint64_t last_word4;   // highest 4-aligned word index w with w + 4 <= exp_words
     uint64_t first_chunk;  // index of this tensor's chunk 0 in the launch
 };
 
@@ -67,7 +69,12 @@ struct LutScratch {
 // Per-wave LDS: the chunk's code words while decoding, then its decoded
 // exponent bytes (4 KB) while storing. A chunk spans at most 4096 * 12 bits;
 // add the alignment slack of the start and the over-read of the last group.
+// Words are staged in reverse order (stream word j at index kRev - j), plus
+// one pad word above, so that one counter gives both the LDS address and the
+// funnel-shift amount of a 32-bit window (see Chain).
 constexpr uint32_t kStageWords = 1568;
+constexpr uint32_t kRev = kStageWords - 1;  // == 3 (mod 4): 16-byte aligned reversed stores
+static_assert(kRev % 4 == 3, "reversed staging needs kRev = 3 mod 4");
 
 // Order LDS traffic between lanes of one wave (no workgroup barrier needed).
 __device__ inline void wave_sync() {
@@ -77,8 +84,10 @@ __device__ inline void wave_sync() {
 }
 
 // Build the decode table of one canonical code: entry i (a 12-bit window of
-// the stream, MSB first) holds (length << 8) | symbol of the code word that
-// starts the window. All 256 threads take part; thread s owns symbol s, then
+// the stream, MSB first) holds (symbol << 8) | length of the code word that
+// starts the window. The length sits in the low bits so that a 32-bit shift
+// by the whole entry consumes exactly the code (the hardware reads only the
+// low 5 bits of a shift amount). All 256 threads take part; thread s owns symbol s, then
 // table entries [16 s, 16 s + 16). Callers bracket it with barriers.
 __device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, LutScratch &S) {
     const int s = threadIdx.x;
@@ -119,144 +128,210 @@ __device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, L
     // that length's first code.
     auto entry = [&](uint32_t idx) -> uint32_t {
         uint32_t l = 1;
-#pragma unroll
         for (uint32_t k = 1; k < kMaxLen; ++k) l += idx >= S.limit[k] ? 1u : 0u;
         const uint32_t j = S.start[l] + ((idx >> (kMaxLen - l)) - S.first[l]);
-        return (l << 8) | S.sorted[j & 255];
+        return ((uint32_t)S.sorted[j & 255] << 8) | l;
     };
     const uint32_t i0 = (uint32_t)s * 16;
     const uint32_t e0 = entry(i0);
-    uint32_t v[8];
-    if ((e0 >> 8) <= 8) {
+    if ((e0 & 0xFF) <= 8) {
         // codes of <= 8 bits own whole 16-aligned blocks of the index space
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = e0 | (e0 << 16);
+        const uint32_t d = e0 | (e0 << 16);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut + i0);
+        dst[0] = make_uint4(d, d, d, d);
+        dst[1] = make_uint4(d, d, d, d);
     } else {
 #pragma unroll 1
-        for (int j = 0; j < 8; ++j) v[j] = entry(i0 + 2 * j) | (entry(i0 + 2 * j + 1) << 16);
+        for (uint32_t j = 0; j < 16; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(lut + i0);
-    dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
-    dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
 }
 
-// Two BF16 values from their sign/mantissa bytes and exponent bytes, each
-// pair given as 16-bit lanes of a dword (element 0 in the low half).
-__device__ inline uint32_t join_pair(uint32_t b2, uint32_t e2) {
-    return (b2 & 0x007F007Fu) | (e2 << 7) | ((b2 & 0x00800080u) << 8);
+// Two BF16 values from the sign/mantissa bytes b and exponent bytes e of
+// elements 0,1 (kHigh: of elements 2,3). With v = [e1 b1 e0 b0], each 16-bit
+// half of v is (e << 8) | (s << 7) | m; the result half is
+// (s << 15) | (e << 7) | m.
+template <bool kHigh>
+__device__ inline uint32_t join_pair(uint32_t b, uint32_t e) {
+    // b2, e2: the two elements' bytes in 16-bit lanes. The result half is
+    // (e << 7) + m + (s << 15) = (e << 7) + b + 255 * (b & 0x80), and no
+    // half overflows into the next.
+    constexpr uint32_t sel = kHigh ? 0x0c030c02u : 0x0c010c00u;
+    const uint32_t b2 = __builtin_amdgcn_perm(0u, b, sel);
+    const uint32_t e2 = __builtin_amdgcn_perm(0u, e, sel);
+    return (e2 << 7) + (__umul24(b2 & 0x00800080u, 255u) + b2);
 }
 
-// Bytes 0,1 (lo) or 2,3 (hi) of x moved into the two 16-bit halves.
-__device__ inline uint32_t spread_lo(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0x0c010c00u); }
-__device__ inline uint32_t spread_hi(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0x0c030c02u); }
+// Symbols (byte 1 of two table entries) packed as bytes 0,1 of a word.
+__device__ inline uint32_t sym_pair(uint32_t e1, uint32_t e2) { return __builtin_amdgcn_perm(e2, e1, 0x0c0c0501u); }
+// Bytes 0,1 of lo and of hi as the four bytes of a word.
+__device__ inline uint32_t join_halves(uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x05040100u); }
 
-// Put the low byte of e into byte k of w.
-template <int k>
-__device__ inline uint32_t put_byte(uint32_t w, uint32_t e) {
-    // selector bytes 4..7 pick w's bytes, 0 picks e's byte 0
-    constexpr uint32_t keep = 0x07060504u;
-    constexpr uint32_t sel = (keep & ~(0xFFu << (8 * k)));
-    return __builtin_amdgcn_perm(w, e, sel);
-}
-
-// One decoding chain: a 64-bit MSB-aligned bit buffer over the staged words.
+// One decoding chain. With P the bit position in the staged words (MSB
+// first), the chain keeps r = 32 * kRev - P. Then the next 32 stream bits are
+// the funnel shift of staged words [r/32 + 1] (high) and [r/32] (low) by
+// r mod 32, and consuming a code of length l is r -= l.
 struct Chain {
-    uint64_t buf;    // next stream bits, MSB first
-    uint32_t avail;  // valid bits in buf (>= 32 at the start of every pair)
-    uint32_t wi;     // staged word that `nxt` came from
-    uint32_t nxt;    // that word, loaded ahead of need
+    uint32_t r;
 };
 
-__device__ inline uint32_t staged(const uint32_t *stage, uint32_t i) {
-    return stage[min(i, kStageWords - 1)];
+__device__ inline uint32_t window(const uint32_t *stage, uint32_t r) {
+    const uint32_t *p = stage + (r >> 5);
+    return __builtin_amdgcn_alignbit(p[1], p[0], r);
 }
 
-__device__ inline void chain_start(Chain &c, const uint32_t *stage, uint32_t bit) {
-    const uint32_t w = bit >> 5, sh = bit & 31;
-    const uint64_t v = ((uint64_t)staged(stage, w) << 32) | staged(stage, w + 1);
-    c.buf = v << sh;
-    c.avail = 64 - sh;
-    c.wi = w + 2;
-    c.nxt = staged(stage, c.wi);
+__device__ inline uint32_t lookup(const uint16_t *lut, uint32_t win) { return lut[win >> (32 - kMaxLen)]; }
+
+// Decode two symbols from one 32-bit window (two codes take at most 24 bits)
+// and return them as bytes 0,1.
+__device__ inline uint32_t chain_pair(Chain &c, const uint32_t *stage, const uint16_t *lut) {
+    const uint32_t win = window(stage, c.r);
+    const uint32_t e1 = lookup(lut, win);
+    const uint32_t e2 = lookup(lut, win << (e1 & 31));
+    c.r -= (e1 + e2) & 0xFF;
+    return sym_pair(e1, e2);
 }
 
-__device__ inline uint32_t lookup(const uint16_t *lut, uint64_t buf) {
-    return lut[(uint32_t)(buf >> (64 - kMaxLen))];
+__device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Where a chunk's code bits lie among the stream words.
+struct ChunkGeom {
+    uint64_t w0;      // first staged stream word (16-byte aligned)
+    uint32_t nwords;  // words to stage: through the chunk's last bit plus over-read slack
+    uint32_t rel;     // the chunk's first bit, counted from word w0
+};
+
+__device__ inline ChunkGeom chunk_geom(uint64_t base, uint64_t end) {
+    ChunkGeom g;
+    g.w0 = (base >> 5) & ~(uint64_t)3;
+    // unsigned arithmetic saturates through the min on a corrupt base pair
+    const uint64_t want = ((end + 31) >> 5) + 16 - g.w0;
+    g.nwords = (uint32_t)umin64(want, kStageWords);
+    g.rel = (uint32_t)(base - (g.w0 << 5));  // < 128
+    return g;
 }
 
-// Decode two symbols, then top the buffer up with one word when it holds
-// fewer than 32 bits (two codes take at most 24).
-template <int k>
-__device__ inline void chain_pair(Chain &c, const uint32_t *stage, const uint16_t *lut, uint32_t &w) {
-    const uint32_t e1 = lookup(lut, c.buf);
-    const uint32_t l1 = e1 >> 8;
-    c.buf <<= l1;
-    const uint32_t e2 = lookup(lut, c.buf);
-    const uint32_t l2 = e2 >> 8;
-    c.buf <<= l2;
-    w = put_byte<k + 1>(put_byte<k>(w, e1), e2);
-    c.avail -= l1 + l2;
-    const bool refill = c.avail < 32;
-    const uint32_t word = refill ? c.nxt : 0u;
-    c.buf |= (uint64_t)word << ((32 - c.avail) & 63);
-    c.avail += refill ? 32u : 0u;
-    c.wi += refill ? 1u : 0u;
-    c.nxt = staged(stage, c.wi);
+// The first 512 staged words of a chunk travel through registers so that
+// their loads can be issued one chunk ahead; longer chunks (more than about
+// 4 bits per element) fetch the rest when they are staged.
+constexpr uint32_t kPrefetchWords = 2 * 4 * kWave;
+
+struct StreamRegs {
+    uint4 v[2];
+};
+
+// Four stream words from 4-aligned index g. Past the end of the section the
+// index is clamped: such words lie beyond the last code bit (the stream ends
+// with four zero words), so what they hold never reaches an output.
+__device__ inline uint4 load_words4(const TensorDesc &T, uint64_t g) {
+    return *reinterpret_cast<const uint4 *>(T.exp + umin64(g, T.last_word4));
 }
 
-// One wave restores chunk `lc` of tensor T.
-__device__ void decode_chunk(const TensorDesc &T, uint64_t lc, const uint16_t *lut, uint32_t *stage, int lane) {
-    const uint64_t e0 = lc * kChunk;
-    const uint32_t ne = (uint32_t)min<uint64_t>(kChunk, T.n - e0);
-    const uint32_t ng = (ne + kGroup - 1) / kGroup;
-    const uint64_t base = T.chunk_base[lc];
-    const uint64_t end = T.chunk_base[lc + 1];
-    const uint64_t w0 = (base >> 5) & ~(uint64_t)3;  // 16-byte aligned start
-    // words to stage: through the chunk's last bit plus over-read slack;
-    // the unsigned arithmetic saturates via min() on corrupt bases
-    const uint64_t want = ((end + 31) >> 5) + 16 - w0;
-    const uint32_t nwords = (uint32_t)min<uint64_t>(want, kStageWords);
+__device__ inline void load_stream(const TensorDesc &T, const ChunkGeom &g, int lane, StreamRegs &s) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) s.v[k] = load_words4(T, g.w0 + 4 * (uint32_t)lane + (uint32_t)k * 4 * kWave);
+}
 
-    // sign/mantissa bytes of this lane's store slots, fetched early
-    const uint8_t *sm = T.signmant + e0;
-    const uint16_t *gap = T.gap + lc * kGroupsPerChunk;
-    const uint32_t ga = (uint32_t)lane, gb = (uint32_t)lane + kWave;
-    const uint32_t gap_a = ga < ng ? gap[ga] : 0u;
-    const uint32_t gap_b = gb < ng ? gap[gb] : 0u;
+// Stream word i goes to index kRev - i (reversed; see Chain).
+__device__ inline void put_words4(uint32_t *stage, uint32_t i, uint4 v) {
+    *reinterpret_cast<uint4 *>(stage + (kRev - 3 - i)) = make_uint4(v.w, v.z, v.y, v.x);
+}
 
-    wave_sync();  // the previous chunk's reads of `stage` are done
-    for (uint32_t i = 4 * (uint32_t)lane; i < nwords; i += 4 * kWave) {
-        const uint64_t g = w0 + i;
-        uint4 v;
-        if (g + 4 <= T.exp_words) {
-            v = *reinterpret_cast<const uint4 *>(T.exp + g);
-        } else {
-            v.x = g < T.exp_words ? T.exp[g] : 0u;
-            v.y = g + 1 < T.exp_words ? T.exp[g + 1] : 0u;
-            v.z = g + 2 < T.exp_words ? T.exp[g + 2] : 0u;
-            v.w = g + 3 < T.exp_words ? T.exp[g + 3] : 0u;
-        }
-        *reinterpret_cast<uint4 *>(stage + i) = v;
+__device__ inline void put_stream(const TensorDesc &T, const ChunkGeom &g, const StreamRegs &s, uint32_t *stage,
+                                  int lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t i = 4 * (uint32_t)lane + (uint32_t)k * 4 * kWave;
+        if (i < g.nwords) put_words4(stage, i, s.v[k]);
     }
-    wave_sync();
+    for (uint32_t i = kPrefetchWords + 4 * (uint32_t)lane; i < g.nwords; i += 4 * kWave)
+        put_words4(stage, i, load_words4(T, g.w0 + i));
+}
 
-    const uint32_t rel = (uint32_t)(base - (w0 << 5));  // < 128
-    Chain A, B;
-    chain_start(A, stage, rel + gap_a);
-    chain_start(B, stage, rel + gap_b);
+__device__ inline uint32_t readlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+
+// Chunk bases are fetched with a vector load (lane 0: start, lane 1: end of
+// chunk lc) so that waiting for them never involves the LDS counter.
+__device__ inline uint64_t load_bases(const TensorDesc &T, uint64_t lc, int lane) {
+    return T.chunk_base[lc + (uint64_t)(lane & 1)];
+}
+__device__ inline ChunkGeom geom_from_lanes(uint64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint64_t base = ((uint64_t)readlane(hi, 0) << 32) | readlane(lo, 0);
+    const uint64_t end = ((uint64_t)readlane(hi, 1) << 32) | readlane(lo, 1);
+    return chunk_geom(base, end);
+}
+
+struct Gaps {
+    uint32_t a, b;  // start of groups lane and lane + 64, relative to the chunk
+};
+
+// Groups past the end of a short last chunk take the last group's gap: they
+// decode something, but nothing they decode is stored.
+__device__ inline Gaps load_gaps(const TensorDesc &T, uint64_t lc, int lane) {
+    const uint32_t ng = (uint32_t)((umin64(kChunk, T.n - lc * kChunk) + kGroup - 1) / kGroup);
+    const uint16_t *gap = T.gap + lc * kGroupsPerChunk;
+    return Gaps{gap[min((uint32_t)lane, ng - 1)], gap[min((uint32_t)lane + kWave, ng - 1)]};
+}
+
+// 16 output bytes; the output is written once and not read back here, so the
+// stores bypass cache allocation (each store instruction covers whole lines).
+__device__ inline void store_out(uint16_t *p, uint4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
+}
+
+__device__ inline uint64_t chunks_of(const TensorDesc &T) { return (T.n + kChunk - 1) / kChunk; }
+
+// A wave's work: chunk lc of the batch's tensor t. Within every tensor the
+// chunks go round the whole grid (wave k of the launch takes chunks k,
+// k + waves, k + 2 waves, ...), so that at any moment the GPU streams one
+// narrow band of each array instead of thousands of far-apart ranges.
+struct Cursor {
+    uint32_t t;   // batch.n_tensors once the wave has no more work
+    uint64_t lc;
+};
+
+__device__ inline void settle(const Batch &B, Cursor &c, uint64_t first) {
+    while (c.t < B.n_tensors && c.lc >= chunks_of(B.t[c.t])) {
+        ++c.t;
+        c.lc = first;
+    }
+}
+
+// Restore one chunk: decode the staged code words, merge with the
+// sign/mantissa bytes, store. `stage` holds the chunk's code words on entry
+// and is free (but for the exponent bytes just written) on exit.
+__device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const ChunkGeom &g, const Gaps &gaps,
+                                     const uint16_t *lut, uint32_t *stage, int lane) {
+    const uint64_t e0 = lc * kChunk;
+    const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
+    const uint8_t *sm = T.signmant + e0;
+    uint2 smv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
+        smv[r] = *reinterpret_cast<const uint2 *>(sm + (i + 8 <= ne ? i : 0));  // tail: reread below
+    }
+
+    // Decode: chain starts clamped so that 32 decodes (at most 384 bits)
+    // never leave the staged words even on a corrupt gap.
+    constexpr uint32_t kMaxStart = 32 * (kRev - 13);
+    Chain A{32 * kRev - min(g.rel + gaps.a, kMaxStart)};
+    Chain B{32 * kRev - min(g.rel + gaps.b, kMaxStart)};
     uint32_t wa[8], wb[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        wa[q] = 0;
-        wb[q] = 0;
-        chain_pair<0>(A, stage, lut, wa[q]);
-        chain_pair<0>(B, stage, lut, wb[q]);
-        chain_pair<2>(A, stage, lut, wa[q]);
-        chain_pair<2>(B, stage, lut, wb[q]);
+        const uint32_t a01 = chain_pair(A, stage, lut);
+        const uint32_t b01 = chain_pair(B, stage, lut);
+        const uint32_t a23 = chain_pair(A, stage, lut);
+        const uint32_t b23 = chain_pair(B, stage, lut);
+        wa[q] = join_halves(a01, a23);
+        wb[q] = join_halves(b01, b23);
     }
     wave_sync();  // every lane is done reading the staged words
-    uint4 *pa = reinterpret_cast<uint4 *>(stage + ga * 8);
-    uint4 *pb = reinterpret_cast<uint4 *>(stage + gb * 8);
+    uint4 *pa = reinterpret_cast<uint4 *>(stage + lane * 8);
+    uint4 *pb = reinterpret_cast<uint4 *>(stage + (lane + kWave) * 8);
     pa[0] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
     pa[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
     pb[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
@@ -264,21 +339,22 @@ __device__ void decode_chunk(const TensorDesc &T, uint64_t lc, const uint16_t *l
     wave_sync();
 
     // Store order: lane handles elements [r*512 + 8*lane, +8) for r = 0..7,
-    // so each store instruction writes 1 KB of consecutive output.
+    // so each store instruction writes 1 KB of output.
     uint16_t *out = T.out + e0;
     const uint8_t *exb = reinterpret_cast<const uint8_t *>(stage);
-#pragma unroll 2
+#pragma unroll
     for (int r = 0; r < 8; ++r) {
         const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
         if (i + 8 <= ne) {
-            const uint2 b = *reinterpret_cast<const uint2 *>(sm + i);
+            const uint2 b = smv[r];
             const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
             uint4 o;
-            o.x = join_pair(spread_lo(b.x), spread_lo(e.x));
-            o.y = join_pair(spread_hi(b.x), spread_hi(e.x));
-            o.z = join_pair(spread_lo(b.y), spread_lo(e.y));
-            o.w = join_pair(spread_hi(b.y), spread_hi(e.y));
-            *reinterpret_cast<uint4 *>(out + i) = o;
+            o.x = join_pair<false>(b.x, e.x);
+            o.y = join_pair<true>(b.x, e.x);
+            o.z = join_pair<false>(b.y, e.y);
+            o.w = join_pair<true>(b.y, e.y);
+            store_out(out + i, o);
+            __builtin_amdgcn_sched_barrier(0);  // keep live ranges per step
         } else {
             for (uint32_t j = i; j < ne && j < i + 8; ++j) {
                 const uint32_t b = sm[j], e = exb[j];
@@ -288,30 +364,78 @@ __device__ void decode_chunk(const TensorDesc &T, uint64_t lc, const uint16_t *l
     }
 }
 
-__global__ __launch_bounds__(kThreads) void afx_decode_kernel(
-    const Batch batch) {
-    __shared__ uint16_t lut[kLutEntries];                     // 8 KB
-    __shared__ uint32_t stage[kWavesPerBlock][kStageWords];   // 24.5 KB
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void afx_decode_kernel(const Batch batch) {
+    __shared__ uint16_t lut[kLutEntries];                        // 8 KB
+    __shared__ uint32_t stage[kWavesPerBlock][kStageWords + 1];  // 24.5 KB
     __shared__ LutScratch scratch;
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const uint64_t total = batch.total_chunks;
-    const uint64_t c_begin = total * blockIdx.x / gridDim.x;
-    const uint64_t c_end = total * (blockIdx.x + 1) / gridDim.x;
+    int lane = threadIdx.x & (kWave - 1);
+    // the wave index is uniform across the wave: keep it (and everything
+    // derived from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t block_first = (uint64_t)blockIdx.x * kWavesPerBlock;
+    const uint64_t first = block_first + (uint64_t)wave;
+    const uint64_t stride = (uint64_t)kWavesPerBlock * gridDim.x;
+    uint32_t *my_stage = stage[wave];
 
-    uint32_t ti = 0;
-    uint64_t c = c_begin;
-    while (c < c_end) {
-        while (ti + 1 < batch.n_tensors && batch.t[ti + 1].first_chunk <= c) ++ti;
-        const TensorDesc &T = batch.t[ti];
-        const uint64_t seg_end = min(c_end, T.first_chunk + (T.n + kChunk - 1) / kChunk);
+    // Stage the wave's first chunk, and start fetching the bases of its second.
+    Cursor cur{0, first};
+    settle(batch, cur, first);
+    Cursor nxt = cur;
+    ChunkGeom g{};
+    Gaps gaps{0, 0};
+    uint64_t next_bases = 0;
+    if (cur.t < batch.n_tensors) {
+        const TensorDesc &T = batch.t[cur.t];
+        g = geom_from_lanes(load_bases(T, cur.lc, lane));
+        gaps = load_gaps(T, cur.lc, lane);
+        StreamRegs s;
+        load_stream(T, g, lane, s);
+        put_stream(T, g, s, my_stage, lane);
+        wave_sync();
+        nxt.lc += stride;
+        settle(batch, nxt, first);
+        if (nxt.t < batch.n_tensors) next_bases = load_bases(batch.t[nxt.t], nxt.lc, lane);
+    }
+
+    for (uint32_t t = 0; t < batch.n_tensors; ++t) {
+        const TensorDesc &T = batch.t[t];
+        if (block_first >= chunks_of(T)) continue;  // no wave of this block has work in T
         __syncthreads();  // all waves are done with the previous table
         build_lut(T.code_len, lut, scratch);
         __syncthreads();
-        for (uint64_t cc = c + (uint64_t)wave; cc < seg_end; cc += kWavesPerBlock)
-            decode_chunk(T, cc - T.first_chunk, lut, stage[wave], lane);
-        c = seg_end;
+        while (cur.t == t) {
+            // recompute per-lane offsets every chunk instead of keeping them
+            // live across the loop
+            asm volatile("" : "+v"(lane));
+            // While chunk `cur` decodes, fetch the code words and gaps of
+            // `nxt` and the bases of the chunk after it.
+            const bool has_next = nxt.t < batch.n_tensors;
+            Cursor nn = nxt;
+            ChunkGeom gn{};
+            StreamRegs sn;
+            Gaps gaps_n{0, 0};
+            if (has_next) {
+                const TensorDesc &Tn = batch.t[nxt.t];
+                gn = geom_from_lanes(next_bases);
+                load_stream(Tn, gn, lane, sn);
+                gaps_n = load_gaps(Tn, nxt.lc, lane);
+                nn.lc += stride;
+                settle(batch, nn, first);
+                next_bases = nn.t < batch.n_tensors ? load_bases(batch.t[nn.t], nn.lc, lane) : 0;
+            }
+            restore_chunk(T, cur.lc, g, gaps, lut, my_stage, lane);
+            if (has_next) {
+                wave_sync();  // the exponent bytes have been read
+                put_stream(batch.t[nxt.t], gn, sn, my_stage, lane);
+                wave_sync();
+                g = gn;
+                gaps = gaps_n;
+            }
+            cur = nxt;
+            nxt = nn;
+        }
     }
 }
 
@@ -364,6 +488,7 @@ TensorDesc describe(const afx_job &j, uint64_t first_chunk) {
     d.out = static_cast<uint16_t *>(j.out_dev);
     d.n = I.n_elems;
     d.exp_words = I.exp_words;
+    d.last_word4 = (I.exp_words - 4) & ~(uint64_t)3;  // exp_words >= 4: the stream ends with 4 zero words
     d.first_chunk = first_chunk;
     return d;
 }
