@@ -166,18 +166,19 @@ def afx_encode_plan(x: np.ndarray, threads: int = 0):
     return lens, bits.value, nbytes.value
 
 
-def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None) -> np.ndarray:
+def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None, plan=None) -> np.ndarray:
     """Encode BF16 bits x into a blob.
 
-    ``out`` may be a numpy uint8 array or a host address (int) with room for
-    the planned size (e.g. pinned memory); the blob bytes are returned as a
-    numpy view when out is an array or None, else the size is returned.
+    ``out`` may be a numpy uint8 array, or an (address, capacity) pair of
+    host memory (e.g. pinned) with room for the planned size; the blob bytes
+    are returned as a numpy view when out is an array or None, else the size
+    is returned. ``plan`` is a result of afx_encode_plan for the same x.
     """
     x = np.ascontiguousarray(x, dtype=np.uint16)
     if shape is None:
         shape = x.shape if x.ndim else (1,)
     x = x.ravel()
-    lens, bits, nbytes = afx_encode_plan(x, threads)
+    lens, bits, nbytes = plan if plan is not None else afx_encode_plan(x, threads)
     shp = (ctypes.c_uint64 * 4)(*(list(shape) + [0] * (4 - len(shape))))
     if out is None:
         out = np.empty(nbytes, np.uint8)

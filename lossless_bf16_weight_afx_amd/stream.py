@@ -1,0 +1,205 @@
+"""Layer-by-layer restore of a compressed model held in pinned host memory.
+
+"Memory requirements of language model inference on a consumer GPU"
+(section "Loading one part of the model at a time") runs a model larger than
+the GPU by loading one part, using it and releasing it before the next;
+"Why Weight Offloading Slows Inference" (section "Loading during
+computation", Figure 2) hides the loading of layer i+1 behind the work on
+layer i. Here the parts are the model's units (embedding, each decoder
+layer, output head with the final norm), stored compressed in pinned host
+memory. Two device buffers alternate: while unit i is restored on the
+compute stream, unit i+1's compressed bytes are copied on a side stream.
+
+The restore itself is libafx's afx_decode_layer_async (one launch per unit);
+this module only moves buffers and orders streams with events.
+"""
+from __future__ import annotations
+
+import time
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import afx, synth
+
+ALIGN = 256
+
+
+def _align(v: int) -> int:
+    return (v + ALIGN - 1) // ALIGN * ALIGN
+
+
+def _out_slot(n: int) -> int:
+    """Elements reserved for an n-element output (keeps every output 256-byte aligned)."""
+    return (n + 127) // 128 * 128
+
+
+@dataclass
+class Unit:
+    """One streamed part: its tensors' blobs packed in one pinned buffer."""
+
+    name: str
+    specs: list
+    host: object  # torch uint8 tensor in pinned memory holding all blobs
+    offsets: list  # byte offset of each tensor's blob in `host`
+    infos: list  # afx_info of each blob
+    n_values: int
+    blob_bytes: int
+    raw: list = field(default_factory=list)  # original bits (optional, for checks)
+
+
+def build_unit(name: str, specs, threads: int = 0, keep_raw: bool = False) -> Unit:
+    """Generate the unit's tensors and encode them into one pinned buffer."""
+    import torch
+
+    xs, plans = [], []
+    for sp in specs:
+        x = synth.generate(sp, threads=threads or None)
+        xs.append(x)
+        plans.append(afx.afx_encode_plan(x, threads))
+    offsets, off = [], 0
+    for plan in plans:
+        offsets.append(off)
+        off = _align(off + plan[2])
+    host = torch.empty(max(off, ALIGN), dtype=torch.uint8, pin_memory=True)
+    base = host.data_ptr()
+    infos = []
+    for sp, x, o, plan in zip(specs, xs, offsets, plans):
+        nbytes = plan[2]
+        n = afx.afx_encode(x, sp.shape, threads=threads, out=(base + o, nbytes), plan=plan)
+        assert n == nbytes
+        infos.append(afx.afx_query(base + o, nbytes))
+    return Unit(name, list(specs), host, offsets, infos, sum(x.size for x in xs), off,
+                raw=xs if keep_raw else [])
+
+
+def build_model(units_specs, threads: int = 0, keep_raw: bool = False, progress=None) -> list:
+    out = []
+    for i, specs in enumerate(units_specs):
+        t0 = time.time()
+        name = specs[0].name.split(".")[0] if len(specs) == 1 else specs[0].name.rsplit(".", 1)[0]
+        u = build_unit(name, specs, threads, keep_raw)
+        out.append(u)
+        if progress:
+            progress(f"[store] unit {i + 1}/{len(units_specs)} {u.name}: {u.n_values} values, "
+                     f"{u.blob_bytes} B compressed, {time.time() - t0:.1f}s")
+    return out
+
+
+class Streamer:
+    """Double-buffered copy-then-restore of a list of units on one GPU."""
+
+    def __init__(self, units, device="cuda"):
+        import torch
+
+        self.torch = torch
+        self.units = units
+        self.dev = torch.device(device)
+        max_blob = max(u.blob_bytes for u in units)
+        max_vals = max(sum(_out_slot(int(i.n_elems)) for i in u.infos) for u in units)
+        self.blob = [torch.empty(max_blob, dtype=torch.uint8, device=self.dev) for _ in range(2)]
+        self.out = [torch.empty(max_vals, dtype=torch.int16, device=self.dev) for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
+        self.jobs = []
+        for u in units:
+            per_buf = []
+            for b in range(2):
+                oo, js = 0, []
+                for info, off in zip(u.infos, u.offsets):
+                    n = int(info.n_elems)
+                    js.append((info, self.blob[b].data_ptr() + off, self.out[b].data_ptr() + 2 * oo, 2 * n))
+                    oo += _out_slot(n)
+                per_buf.append(afx.make_jobs(js))
+            self.jobs.append(per_buf)
+
+    def run(self, on_unit=None) -> dict:
+        """Stream every unit once. ``on_unit(i, unit, out_tensor)`` is called
+        after unit i is restored (it synchronizes; use only off the clock)."""
+        torch = self.torch
+        n = len(self.units)
+        main = torch.cuda.current_stream(self.dev)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        copied = [ev() for _ in range(n)]
+        dec_start = [ev() for _ in range(n)]
+        decoded = [ev() for _ in range(n)]
+        start = ev()
+        torch.cuda.synchronize(self.dev)
+        start.record(main)
+        self.copy_stream.wait_event(start)
+        for i, u in enumerate(self.units):
+            b = i % 2
+            with torch.cuda.stream(self.copy_stream):
+                if i >= 2:
+                    self.copy_stream.wait_event(decoded[i - 2])  # buffer b is free again
+                self.blob[b][:u.blob_bytes].copy_(u.host[:u.blob_bytes], non_blocking=True)
+                copied[i].record(self.copy_stream)
+            main.wait_event(copied[i])
+            dec_start[i].record(main)
+            afx.afx_decode_layer_async(self.jobs[i][b], main.cuda_stream)
+            decoded[i].record(main)
+            if on_unit is not None:
+                decoded[i].synchronize()
+                on_unit(i, u, self.out[b])
+        torch.cuda.synchronize(self.dev)
+        e2e_ms = start.elapsed_time(decoded[-1])
+        dec_ms = [s.elapsed_time(e) for s, e in zip(dec_start, decoded)]
+        return {"e2e_ms": e2e_ms, "decode_ms": dec_ms, "restored_bytes": 2 * sum(u.n_values for u in self.units),
+                "blob_bytes": sum(u.blob_bytes for u in self.units)}
+
+    def link_copy_ms(self) -> float:
+        """Time plain pinned-to-device copies of every unit's compressed bytes."""
+        torch = self.torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(self.dev)
+        s.record(self.copy_stream)
+        with torch.cuda.stream(self.copy_stream):
+            for i, u in enumerate(self.units):
+                self.blob[i % 2][:u.blob_bytes].copy_(u.host[:u.blob_bytes], non_blocking=True)
+        e.record(self.copy_stream)
+        torch.cuda.synchronize(self.dev)
+        return s.elapsed_time(e)
+
+
+def check_unit(u: Unit, out) -> bool:
+    """Bit-exact check of a restored unit against its original bits."""
+    import torch
+
+    off, ok = 0, True
+    for x in u.raw:
+        ref = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(out.device)
+        ok &= bool(torch.equal(out[off:off + x.size], ref))
+        off += _out_slot(x.size)
+    return ok
+
+
+def resident_decode_ms(units, steps: int = 3, device="cuda") -> float:
+    """Restore every unit back to back with all compressed bytes already in
+    HBM (two alternating output buffers); milliseconds per whole-model pass."""
+    import torch
+
+    dev = torch.device(device)
+    blobs = [u.host[:u.blob_bytes].to(dev) for u in units]
+    max_vals = max(sum(_out_slot(int(i.n_elems)) for i in u.infos) for u in units)
+    outs = [torch.empty(max_vals, dtype=torch.int16, device=dev) for _ in range(2)]
+    jobs = []
+    for k, u in enumerate(units):
+        oo, js = 0, []
+        for info, off in zip(u.infos, u.offsets):
+            n = int(info.n_elems)
+            js.append((info, blobs[k].data_ptr() + off, outs[k % 2].data_ptr() + 2 * oo, 2 * n))
+            oo += _out_slot(n)
+        jobs.append(afx.make_jobs(js))
+    s = torch.cuda.current_stream(dev)
+    for j in jobs:  # warm-up pass
+        afx.afx_decode_layer_async(j, s.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(s)
+    for _ in range(steps):
+        for j in jobs:
+            afx.afx_decode_layer_async(j, s.cuda_stream)
+    e1.record(s)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    del blobs, outs
+    return ms

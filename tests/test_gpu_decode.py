@@ -191,3 +191,32 @@ def test_embedding_full_size():
     say("[gpu] case embedding 151936x5120")
     afx.afx_decode_tensor(info, dev.data_ptr(), out.data_ptr(), 2 * x.size, torch.cuda.current_stream().cuda_stream)
     assert torch.equal(out, xd)
+
+
+def test_streamed_units_double_buffered():
+    """Units copied from pinned host memory on a side stream while the
+    previous unit is restored; every unit bit-exact."""
+    from lossless_bf16_weight_afx_amd import stream
+
+    T = synth.TensorSpec
+    units_specs = [
+        [T("u0.w", (2000, 517), "normal", 11), T("u0.norm", (5120,), "normal", 12, 1.0, 0.05)],
+        [T("u1.w", (1024, 4096), "t4", 13)],
+        [T("u2.a", (777, 33), "normal", 14), T("u2.b", (4096,), "normal", 15), T("u2.c", (128,), "normal", 16, 1.0, 0.05)],
+        [T("u3.w", (3000, 1000), "normal", 17)],
+        [T("u4.w", (50, 4096), "t4", 18)],
+    ]
+    say("[gpu] case streamed units: build store")
+    units = stream.build_model(units_specs, threads=8, keep_raw=True)
+    st = stream.Streamer(units)
+    ok = []
+    say("[gpu] case streamed units: checked pass")
+    st.run(on_unit=lambda i, u, out: ok.append(stream.check_unit(u, out)))
+    assert ok == [True] * len(units)
+    say("[gpu] case streamed units: free-running pass")
+    res = st.run()
+    torch.cuda.synchronize()
+    # the last two units are still in their buffers after a free-running pass
+    assert stream.check_unit(units[-1], st.out[(len(units) - 1) % 2])
+    assert stream.check_unit(units[-2], st.out[(len(units) - 2) % 2])
+    assert res["e2e_ms"] > 0 and len(res["decode_ms"]) == len(units)
