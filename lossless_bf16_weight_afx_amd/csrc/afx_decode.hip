@@ -283,19 +283,47 @@ __device__ inline void store_out(uint16_t *p, uint4 v) {
 
 __device__ inline uint64_t chunks_of(const TensorDesc &T) { return (T.n + kChunk - 1) / kChunk; }
 
-// A wave's work: chunk lc of the batch's tensor t. Within every tensor the
-// chunks go round the whole grid (wave k of the launch takes chunks k,
-// k + waves, k + 2 waves, ...), so that at any moment the GPU streams one
-// narrow band of each array instead of thousands of far-apart ranges.
+// A wave's work: chunk lc of the batch's tensor t. The grid is split among
+// the tensors in proportion to their chunk counts, so that a block serves
+// about one tensor (one decode table to build); a tensor too small for a
+// block of its own is served by the block at its position. Within a tensor
+// the chunks go round its blocks (wave k of them takes chunks k, k + waves,
+// ...), so that at any moment each array is streamed in one narrow band.
+constexpr uint64_t kNone = ~(uint64_t)0;
+
 struct Cursor {
-    uint32_t t;   // batch.n_tensors once the wave has no more work
-    uint64_t lc;
+    uint32_t t;       // batch.n_tensors once the wave has no more work
+    uint64_t lc;      // kNone: not yet placed in tensor t
+    uint64_t stride;  // chunks between this wave's consecutive chunks of t
 };
 
-__device__ inline void settle(const Batch &B, Cursor &c, uint64_t first) {
-    while (c.t < B.n_tensors && c.lc >= chunks_of(B.t[c.t])) {
+// Blocks [lo, hi) of the grid serve tensor t; block b is the k-th of nb.
+__device__ inline bool block_share(const Batch &B, uint32_t t, uint64_t b, uint64_t &k, uint64_t &nb) {
+    const uint64_t grid = gridDim.x, total = B.total_chunks;
+    const uint64_t p0 = B.t[t].first_chunk, p1 = p0 + chunks_of(B.t[t]);
+    const uint64_t lo = grid * p0 / total;
+    uint64_t hi = grid * p1 / total;
+    if (hi <= lo) hi = lo + 1;
+    if (b < lo || b >= hi) return false;
+    k = b - lo;
+    nb = hi - lo;
+    return true;
+}
+
+__device__ inline void settle(const Batch &B, Cursor &c, uint64_t b, int wave) {
+    while (c.t < B.n_tensors) {
+        if (c.lc == kNone) {
+            uint64_t k, nb;
+            if (!block_share(B, c.t, b, k, nb)) {
+                ++c.t;
+                continue;
+            }
+            c.lc = k * kWavesPerBlock + (uint64_t)wave;
+            c.stride = nb * kWavesPerBlock;
+        }
+        if (c.lc < chunks_of(B.t[c.t])) return;
         ++c.t;
-        c.lc = first;
+        c.lc = kNone;
     }
 }
 
@@ -374,14 +402,12 @@ void afx_decode_kernel(const Batch batch) {
     // the wave index is uniform across the wave: keep it (and everything
     // derived from it) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint64_t block_first = (uint64_t)blockIdx.x * kWavesPerBlock;
-    const uint64_t first = block_first + (uint64_t)wave;
-    const uint64_t stride = (uint64_t)kWavesPerBlock * gridDim.x;
+    const uint64_t b = blockIdx.x;
     uint32_t *my_stage = stage[wave];
 
     // Stage the wave's first chunk, and start fetching the bases of its second.
-    Cursor cur{0, first};
-    settle(batch, cur, first);
+    Cursor cur{0, kNone, 0};
+    settle(batch, cur, b, wave);
     Cursor nxt = cur;
     ChunkGeom g{};
     Gaps gaps{0, 0};
@@ -394,14 +420,16 @@ void afx_decode_kernel(const Batch batch) {
         load_stream(T, g, lane, s);
         put_stream(T, g, s, my_stage, lane);
         wave_sync();
-        nxt.lc += stride;
-        settle(batch, nxt, first);
+        nxt.lc += nxt.stride;
+        settle(batch, nxt, b, wave);
         if (nxt.t < batch.n_tensors) next_bases = load_bases(batch.t[nxt.t], nxt.lc, lane);
     }
 
     for (uint32_t t = 0; t < batch.n_tensors; ++t) {
         const TensorDesc &T = batch.t[t];
-        if (block_first >= chunks_of(T)) continue;  // no wave of this block has work in T
+        uint64_t k, nb;
+        if (!block_share(batch, t, b, k, nb) || k * kWavesPerBlock >= chunks_of(T))
+            continue;  // no wave of this block has work in T
         __syncthreads();  // all waves are done with the previous table
         build_lut(T.code_len, lut, scratch);
         __syncthreads();
@@ -421,8 +449,8 @@ void afx_decode_kernel(const Batch batch) {
                 gn = geom_from_lanes(next_bases);
                 load_stream(Tn, gn, lane, sn);
                 gaps_n = load_gaps(Tn, nxt.lc, lane);
-                nn.lc += stride;
-                settle(batch, nn, first);
+                nn.lc += nn.stride;
+                settle(batch, nn, b, wave);
                 next_bases = nn.t < batch.n_tensors ? load_bases(batch.t[nn.t], nn.lc, lane) : 0;
             }
             restore_chunk(T, cur.lc, g, gaps, lut, my_stage, lane);
