@@ -226,9 +226,13 @@ __device__ inline uint4 load_words4(const TensorDesc &T, uint64_t g) {
     return *reinterpret_cast<const uint4 *>(T.exp + umin64(g, T.last_word4));
 }
 
+// Only the words the chunk needs are requested (typical chunks need ~350).
 __device__ inline void load_stream(const TensorDesc &T, const ChunkGeom &g, int lane, StreamRegs &s) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) s.v[k] = load_words4(T, g.w0 + 4 * (uint32_t)lane + (uint32_t)k * 4 * kWave);
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t i = 4 * (uint32_t)lane + (uint32_t)k * 4 * kWave;
+        if (i < g.nwords) s.v[k] = load_words4(T, g.w0 + i);
+    }
 }
 
 // Stream word i goes to index kRev - i (reversed; see Chain).
@@ -405,24 +409,18 @@ void afx_decode_kernel(const Batch batch) {
     const uint64_t b = blockIdx.x;
     uint32_t *my_stage = stage[wave];
 
-    // Stage the wave's first chunk, and start fetching the bases of its second.
+    // Start fetching the wave's first chunk (its bases and gaps); it is
+    // staged after the first decode table is built, which hides these loads.
     Cursor cur{0, kNone, 0};
     settle(batch, cur, b, wave);
     Cursor nxt = cur;
     ChunkGeom g{};
     Gaps gaps{0, 0};
     uint64_t next_bases = 0;
+    bool staged = false;
     if (cur.t < batch.n_tensors) {
-        const TensorDesc &T = batch.t[cur.t];
-        g = geom_from_lanes(load_bases(T, cur.lc, lane));
-        gaps = load_gaps(T, cur.lc, lane);
-        StreamRegs s;
-        load_stream(T, g, lane, s);
-        put_stream(T, g, s, my_stage, lane);
-        wave_sync();
-        nxt.lc += nxt.stride;
-        settle(batch, nxt, b, wave);
-        if (nxt.t < batch.n_tensors) next_bases = load_bases(batch.t[nxt.t], nxt.lc, lane);
+        next_bases = load_bases(batch.t[cur.t], cur.lc, lane);
+        gaps = load_gaps(batch.t[cur.t], cur.lc, lane);
     }
 
     for (uint32_t t = 0; t < batch.n_tensors; ++t) {
@@ -433,6 +431,18 @@ void afx_decode_kernel(const Batch batch) {
         __syncthreads();  // all waves are done with the previous table
         build_lut(T.code_len, lut, scratch);
         __syncthreads();
+        if (!staged && cur.t == t) {
+            // stage the wave's first chunk; start the bases of its second
+            g = geom_from_lanes(next_bases);
+            StreamRegs s;
+            load_stream(T, g, lane, s);
+            put_stream(T, g, s, my_stage, lane);
+            wave_sync();
+            nxt.lc += nxt.stride;
+            settle(batch, nxt, b, wave);
+            next_bases = nxt.t < batch.n_tensors ? load_bases(batch.t[nxt.t], nxt.lc, lane) : 0;
+            staged = true;
+        }
         while (cur.t == t) {
             // recompute per-lane offsets every chunk instead of keeping them
             // live across the loop
@@ -537,8 +547,12 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
     int max_blocks = 0;
     int rc = max_blocks_for_current_device(&max_blocks);
     if (rc != AFX_OK) return rc;
-    const uint64_t want = (total + kWavesPerBlock - 1) / kWavesPerBlock;
-    const unsigned grid = (unsigned)std::min<uint64_t>(want, (uint64_t)max_blocks);
+    // Every wave should get the same number of chunks, or the launch ends with
+    // part of the grid idle: with at most max_blocks blocks each wave takes
+    // ceil(total / (4 max_blocks)) chunks; use just enough blocks for that.
+    const uint64_t per_wave = (total + (uint64_t)kWavesPerBlock * max_blocks - 1) / ((uint64_t)kWavesPerBlock * max_blocks);
+    const uint64_t want = (total + (uint64_t)kWavesPerBlock * per_wave - 1) / ((uint64_t)kWavesPerBlock * per_wave);
+    const unsigned grid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)max_blocks));
     hipLaunchKernelGGL(afx_decode_kernel, dim3(grid), dim3(kThreads), 0, stream, batch);
     return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
 }
