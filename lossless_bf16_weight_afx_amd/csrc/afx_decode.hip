@@ -339,11 +339,16 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
     const uint64_t e0 = lc * kChunk;
     const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
     const uint8_t *sm = T.signmant + e0;
+    // Sign/mantissa bytes are read exactly once: load them without keeping
+    // them in the caches (the code words stay cached: neighbouring chunks
+    // share the lines at their ends).
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     uint2 smv[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
-        smv[r] = *reinterpret_cast<const uint2 *>(sm + (i + 8 <= ne ? i : 0));  // tail: reread below
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sm + (i + 8 <= ne ? i : 0)));
+        smv[r] = make_uint2(t.x, t.y);  // tail elements are reread below
     }
 
     // Decode: chain starts clamped so that 32 decodes (at most 384 bits)
