@@ -274,7 +274,9 @@ struct Gaps {
 __device__ inline Gaps load_gaps(const TensorDesc &T, uint64_t lc, int lane) {
     const uint32_t ng = (uint32_t)((umin64(kChunk, T.n - lc * kChunk) + kGroup - 1) / kGroup);
     const uint16_t *gap = T.gap + lc * kGroupsPerChunk;
-    return Gaps{gap[min((uint32_t)lane, ng - 1)], gap[min((uint32_t)lane + kWave, ng - 1)]};
+    // read once: not kept in the caches
+    return Gaps{__builtin_nontemporal_load(gap + min((uint32_t)lane, ng - 1)),
+                __builtin_nontemporal_load(gap + min((uint32_t)lane + kWave, ng - 1))};
 }
 
 // 16 output bytes; the output is written once and not read back here, so the
