@@ -193,7 +193,7 @@ def main() -> int:
 
     achieved = traffic_pass / (launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(args.workload),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(workload),
                 "algorithmic_bytes_per_launch": traffic_pass, "kernel": KERNEL_NAME,
                 "kernel_ms": round(launch_ms, 5), "copy_ceiling_GBps": round(copy_gbps, 1)}
 

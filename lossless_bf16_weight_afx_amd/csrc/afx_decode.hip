@@ -8,16 +8,23 @@
 // bytes reach device memory.
 //
 // Work decomposition (one launch per batch of up to 32 tensors):
-//   * the batch's chunks (4096 elements each) are numbered globally; each
-//     workgroup (4 wave64s) takes one contiguous range of chunks;
-//   * for every tensor its range touches, the workgroup builds the 4096-entry
-//     decode table (u16: length << 8 | symbol) of that tensor's canonical code
-//     in LDS, from the 256 code lengths alone;
-//   * each wave restores one chunk at a time: it stages the chunk's code words
-//     in its own LDS slice with 16-byte loads; lane j then decodes groups j and
-//     j + 64 (32 symbols each, two independent dependency chains) from a 64-bit
-//     MSB-aligned bit buffer, peeking 12 bits per symbol into the table and
-//     topping the buffer up with one prefetched word after every two symbols;
+//   * one workgroup of 16 wave64s fills a CU (4 waves per SIMD). The grid
+//     is split among the batch's tensors in proportion to their chunk
+//     (4096-element) counts, so a workgroup serves about one tensor; within
+//     a tensor the chunks go round its workgroups, so that all of them move
+//     through each array together, in one narrow band;
+//   * the waves of a workgroup claim its chunks one at a time from a counter
+//     in LDS. A SIMD issues for its oldest waves first, so waves run at
+//     different speeds; claiming keeps them finishing together;
+//   * for every tensor it serves, the workgroup builds the 4096-entry decode
+//     table (u16: symbol << 8 | length) of that tensor's canonical code in
+//     LDS, from the 256 code lengths alone;
+//   * each wave restores one chunk at a time, software-pipelined: while chunk
+//     i decodes, the code words and gap offsets of chunk i + 1 and the bit
+//     bases of chunk i + 2 are in flight. The code words are staged in the
+//     wave's own LDS slice; lane j then decodes groups j and j + 64 (32
+//     symbols each, two independent dependency chains), two symbols per
+//     32-bit window of the staged stream;
 //   * decoded exponent bytes go back to the wave's LDS slice in element order;
 //     the wave re-reads them in store order, merges them with the
 //     sign/mantissa bytes and writes 16-byte stores, 1 KB per instruction.
@@ -33,8 +40,9 @@ namespace afx {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kWavesPerEU = 4;  // occupancy target: LDS allows 4 blocks of 4 waves per CU
+constexpr int kWavesPerBlock = 16;  // one workgroup fills a CU (4 waves per SIMD)
+constexpr int kWavesPerEU = 4;
+constexpr int kSymbolWaves = 256 / kWave;  // waves that hold one exponent value per lane
 constexpr int kThreads = kWave * kWavesPerBlock;
 constexpr int kLutEntries = 1 << kMaxLen;  // 4096
 
@@ -59,7 +67,7 @@ struct Batch {
 };
 
 struct LutScratch {
-    uint32_t wave_count[kWavesPerBlock][kMaxLen + 1];
+    uint32_t wave_count[kSymbolWaves][kMaxLen + 1];
     uint32_t limit[kMaxLen + 1];  // end of each length's slice of the 12-bit index space
     uint32_t first[kMaxLen + 1];  // first canonical code of each length
     uint32_t start[kMaxLen + 1];  // position of that length's first symbol in `sorted`
@@ -75,6 +83,9 @@ struct LutScratch {
 constexpr uint32_t kStageWords = 1568;
 constexpr uint32_t kRev = kStageWords - 1;  // == 3 (mod 4): 16-byte aligned reversed stores
 static_assert(kRev % 4 == 3, "reversed staging needs kRev = 3 mod 4");
+// Each wave's slice, with the pad word, rounded up to 16 bytes so that every
+// slice starts 16-byte aligned.
+constexpr uint32_t kStageRow = (kStageWords + 1 + 3) & ~3u;
 
 // Order LDS traffic between lanes of one wave (no workgroup barrier needed).
 __device__ inline void wave_sync() {
@@ -87,27 +98,30 @@ __device__ inline void wave_sync() {
 // the stream, MSB first) holds (symbol << 8) | length of the code word that
 // starts the window. The length sits in the low bits so that a 32-bit shift
 // by the whole entry consumes exactly the code (the hardware reads only the
-// low 5 bits of a shift amount). All 256 threads take part; thread s owns symbol s, then
-// table entries [16 s, 16 s + 16). Callers bracket it with barriers.
+// low 5 bits of a shift amount). All 1024 threads take part: thread s < 256
+// owns symbol s, then every thread s fills table entries [4 s, 4 s + 4).
+// Callers bracket it with barriers.
 __device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, LutScratch &S) {
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1), wave = s / kWave;
-    uint32_t len = code_len[s];
-    if (len > kMaxLen) len = 0;  // only a corrupt blob gets here; treat as unused
-
+    uint32_t len = 0;
     uint32_t rank = 0;  // among same-length symbols of this wave with smaller value
+    if (wave < kSymbolWaves) {
+        len = code_len[s];
+        if (len > kMaxLen) len = 0;  // only a corrupt blob gets here; treat as unused
 #pragma unroll
-    for (uint32_t l = 1; l <= kMaxLen; ++l) {
-        const uint64_t m = __ballot(len == l);
-        if (len == l) rank = (uint32_t)__popcll(m & ((1ull << lane) - 1));
-        if (lane == 0) S.wave_count[wave][l] = (uint32_t)__popcll(m);
+        for (uint32_t l = 1; l <= kMaxLen; ++l) {
+            const uint64_t m = __ballot(len == l);
+            if (len == l) rank = (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (lane == 0) S.wave_count[wave][l] = (uint32_t)__popcll(m);
+        }
     }
     __syncthreads();
     if (s == 0) {
         uint32_t code = 0, pos = 0;
         for (uint32_t l = 1; l <= kMaxLen; ++l) {
             uint32_t cnt = 0;
-            for (int w = 0; w < kWavesPerBlock; ++w) cnt += S.wave_count[w][l];
+            for (int w = 0; w < kSymbolWaves; ++w) cnt += S.wave_count[w][l];
             S.first[l] = code;
             S.start[l] = pos;
             S.limit[l] = (code + cnt) << (kMaxLen - l);
@@ -132,17 +146,16 @@ __device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, L
         const uint32_t j = S.start[l] + ((idx >> (kMaxLen - l)) - S.first[l]);
         return ((uint32_t)S.sorted[j & 255] << 8) | l;
     };
-    const uint32_t i0 = (uint32_t)s * 16;
+    constexpr uint32_t kPer = kLutEntries / kThreads;  // 4 entries per thread
+    const uint32_t i0 = (uint32_t)s * kPer;
     const uint32_t e0 = entry(i0);
-    if ((e0 & 0xFF) <= 8) {
-        // codes of <= 8 bits own whole 16-aligned blocks of the index space
+    if ((e0 & 0xFF) <= kMaxLen - 2) {
+        // a code of <= 10 bits owns whole 4-aligned blocks of the index space
         const uint32_t d = e0 | (e0 << 16);
-        uint4 *dst = reinterpret_cast<uint4 *>(lut + i0);
-        dst[0] = make_uint4(d, d, d, d);
-        dst[1] = make_uint4(d, d, d, d);
+        *reinterpret_cast<uint2 *>(lut + i0) = make_uint2(d, d);
     } else {
-#pragma unroll 1
-        for (uint32_t j = 0; j < 16; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
+#pragma unroll
+        for (uint32_t j = 0; j < kPer; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
     }
 }
 
@@ -289,21 +302,12 @@ __device__ inline void store_out(uint16_t *p, uint4 v) {
 
 __device__ inline uint64_t chunks_of(const TensorDesc &T) { return (T.n + kChunk - 1) / kChunk; }
 
-// A wave's work: chunk lc of the batch's tensor t. The grid is split among
-// the tensors in proportion to their chunk counts, so that a block serves
-// about one tensor (one decode table to build); a tensor too small for a
-// block of its own is served by the block at its position. Within a tensor
-// the chunks go round its blocks (wave k of them takes chunks k, k + waves,
-// ...), so that at any moment each array is streamed in one narrow band.
-constexpr uint64_t kNone = ~(uint64_t)0;
-
-struct Cursor {
-    uint32_t t;       // batch.n_tensors once the wave has no more work
-    uint64_t lc;      // kNone: not yet placed in tensor t
-    uint64_t stride;  // chunks between this wave's consecutive chunks of t
-};
-
-// Blocks [lo, hi) of the grid serve tensor t; block b is the k-th of nb.
+// The grid is split among the tensors in proportion to their chunk counts,
+// so that a workgroup serves about one tensor (one decode table to build); a
+// tensor too small for a workgroup of its own is served by the workgroup at
+// its position. Within a tensor the chunks go round its workgroups (the k-th
+// of nb takes chunks k, k + nb, k + 2 nb, ...), so that at any moment each
+// array is streamed in one narrow band. Blocks [lo, hi) serve tensor t.
 __device__ inline bool block_share(const Batch &B, uint32_t t, uint64_t b, uint64_t &k, uint64_t &nb) {
     const uint64_t grid = gridDim.x, total = B.total_chunks;
     const uint64_t p0 = B.t[t].first_chunk, p1 = p0 + chunks_of(B.t[t]);
@@ -316,28 +320,12 @@ __device__ inline bool block_share(const Batch &B, uint32_t t, uint64_t b, uint6
     return true;
 }
 
-__device__ inline void settle(const Batch &B, Cursor &c, uint64_t b, int wave) {
-    while (c.t < B.n_tensors) {
-        if (c.lc == kNone) {
-            uint64_t k, nb;
-            if (!block_share(B, c.t, b, k, nb)) {
-                ++c.t;
-                continue;
-            }
-            c.lc = k * kWavesPerBlock + (uint64_t)wave;
-            c.stride = nb * kWavesPerBlock;
-        }
-        if (c.lc < chunks_of(B.t[c.t])) return;
-        ++c.t;
-        c.lc = kNone;
-    }
-}
-
 // Restore one chunk: decode the staged code words, merge with the
 // sign/mantissa bytes, store. `stage` holds the chunk's code words on entry
 // and is free (but for the exponent bytes just written) on exit.
 __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const ChunkGeom &g, const Gaps &gaps,
-                                     const uint16_t *lut, uint32_t *stage, int lane) {
+                                     const uint16_t *lut, uint32_t *stage, int lane, uint64_t later_bases,
+                                     ChunkGeom &later) {
     const uint64_t e0 = lc * kChunk;
     const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
     const uint8_t *sm = T.signmant + e0;
@@ -376,6 +364,12 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
     pb[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
     pb[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
     wave_sync();
+    // Read out the bases fetched for a later chunk now, while the only loads
+    // issued after them are this chunk's sign/mantissa bytes (needed next
+    // anyway): read after the stores below, they would make the wave wait
+    // for those stores to complete.
+    asm volatile("" : "+v"(later_bases));  // not before the decode above
+    later = geom_from_lanes(later_bases);
 
     // Store order: lane handles elements [r*512 + 8*lane, +8) for r = 0..7,
     // so each store instruction writes 1 KB of output.
@@ -405,81 +399,85 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void afx_decode_kernel(const Batch batch) {
-    __shared__ uint16_t lut[kLutEntries];                        // 8 KB
-    __shared__ uint32_t stage[kWavesPerBlock][kStageWords + 1];  // 24.5 KB
+    __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];  // 8 KB
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][kStageRow];  // 98 KB
     __shared__ LutScratch scratch;
+    __shared__ uint32_t next_j;  // the workgroup's next unclaimed chunk of the tensor
 
     int lane = threadIdx.x & (kWave - 1);
     // the wave index is uniform across the wave: keep it (and everything
     // derived from it) in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint64_t b = blockIdx.x;
     uint32_t *my_stage = stage[wave];
-
-    // Start fetching the wave's first chunk (its bases and gaps); it is
-    // staged after the first decode table is built, which hides these loads.
-    Cursor cur{0, kNone, 0};
-    settle(batch, cur, b, wave);
-    Cursor nxt = cur;
-    ChunkGeom g{};
-    Gaps gaps{0, 0};
-    uint64_t next_bases = 0;
-    bool staged = false;
-    if (cur.t < batch.n_tensors) {
-        next_bases = load_bases(batch.t[cur.t], cur.lc, lane);
-        gaps = load_gaps(batch.t[cur.t], cur.lc, lane);
-    }
 
     for (uint32_t t = 0; t < batch.n_tensors; ++t) {
         const TensorDesc &T = batch.t[t];
         uint64_t k, nb;
-        if (!block_share(batch, t, b, k, nb) || k * kWavesPerBlock >= chunks_of(T))
-            continue;  // no wave of this block has work in T
-        __syncthreads();  // all waves are done with the previous table
-        build_lut(T.code_len, lut, scratch);
+        if (!block_share(batch, t, b, k, nb) || k >= chunks_of(T)) continue;
+        // The workgroup's chunks of T, j = 0, 1, ...: chunk k + j nb. Wave w
+        // starts with j = w and j = w + 16; after that each wave claims the
+        // next unclaimed j when it starts a chunk, so waves that the SIMDs
+        // serve faster restore more chunks and all finish together.
+        const uint64_t mine = (chunks_of(T) - k + nb - 1) / nb;
+        uint64_t jc = wave, jn = wave + kWavesPerBlock;
+        const bool has_c = jc < mine;
+        bool has_n = jn < mine;
+        // start fetching the first two chunks' bases and the first one's
+        // gaps; building the decode table hides these loads
+        uint64_t bases_c = 0, bases_n = 0;
+        Gaps gaps{0, 0};
+        if (has_c) {
+            bases_c = load_bases(T, k + jc * nb, lane);
+            gaps = load_gaps(T, k + jc * nb, lane);
+        }
+        if (has_n) bases_n = load_bases(T, k + jn * nb, lane);
+        __syncthreads();  // every wave is done with the previous table and counter
+        if (threadIdx.x == 0) next_j = 2 * kWavesPerBlock;
+        build_lut(T.code_len, lut, scratch);  // ends with a barrier
         __syncthreads();
-        if (!staged && cur.t == t) {
-            // stage the wave's first chunk; start the bases of its second
-            g = geom_from_lanes(next_bases);
+        if (!has_c) continue;
+
+        ChunkGeom g = geom_from_lanes(bases_c);
+        {
             StreamRegs s;
             load_stream(T, g, lane, s);
             put_stream(T, g, s, my_stage, lane);
             wave_sync();
-            nxt.lc += nxt.stride;
-            settle(batch, nxt, b, wave);
-            next_bases = nxt.t < batch.n_tensors ? load_bases(batch.t[nxt.t], nxt.lc, lane) : 0;
-            staged = true;
         }
-        while (cur.t == t) {
+        ChunkGeom gn = geom_from_lanes(bases_n);
+        while (true) {
             // recompute per-lane offsets every chunk instead of keeping them
             // live across the loop
             asm volatile("" : "+v"(lane));
-            // While chunk `cur` decodes, fetch the code words and gaps of
-            // `nxt` and the bases of the chunk after it.
-            const bool has_next = nxt.t < batch.n_tensors;
-            Cursor nn = nxt;
-            ChunkGeom gn{};
+            // While chunk jc decodes, fetch the code words and gaps of jn,
+            // claim the chunk after it and fetch that one's bases.
+            uint64_t jnn = ~(uint64_t)0;
+            bool has_nn = false;
             StreamRegs sn;
             Gaps gaps_n{0, 0};
-            if (has_next) {
-                const TensorDesc &Tn = batch.t[nxt.t];
-                gn = geom_from_lanes(next_bases);
-                load_stream(Tn, gn, lane, sn);
-                gaps_n = load_gaps(Tn, nxt.lc, lane);
-                nn.lc += nn.stride;
-                settle(batch, nn, b, wave);
-                next_bases = nn.t < batch.n_tensors ? load_bases(batch.t[nn.t], nn.lc, lane) : 0;
+            uint64_t bases_nn = 0;
+            if (has_n) {
+                uint32_t v = 0;
+                if (lane == 0) v = atomicAdd(&next_j, 1u);
+                jnn = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+                has_nn = jnn < mine;
+                load_stream(T, gn, lane, sn);
+                gaps_n = load_gaps(T, k + jn * nb, lane);
+                if (has_nn) bases_nn = load_bases(T, k + jnn * nb, lane);
             }
-            restore_chunk(T, cur.lc, g, gaps, lut, my_stage, lane);
-            if (has_next) {
-                wave_sync();  // the exponent bytes have been read
-                put_stream(batch.t[nxt.t], gn, sn, my_stage, lane);
-                wave_sync();
-                g = gn;
-                gaps = gaps_n;
-            }
-            cur = nxt;
-            nxt = nn;
+            ChunkGeom gnn;
+            restore_chunk(T, k + jc * nb, g, gaps, lut, my_stage, lane, bases_nn, gnn);
+            if (!has_n) break;
+            wave_sync();  // the exponent bytes have been read
+            put_stream(T, gn, sn, my_stage, lane);
+            wave_sync();
+            g = gn;
+            gaps = gaps_n;
+            gn = gnn;
+            jc = jn;
+            jn = jnn;
+            has_n = has_nn;
         }
     }
 }
@@ -554,11 +552,11 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
     int max_blocks = 0;
     int rc = max_blocks_for_current_device(&max_blocks);
     if (rc != AFX_OK) return rc;
-    // Every wave should get the same number of chunks, or the launch ends with
-    // part of the grid idle: with at most max_blocks blocks each wave takes
-    // ceil(total / (4 max_blocks)) chunks; use just enough blocks for that.
-    const uint64_t per_wave = (total + (uint64_t)kWavesPerBlock * max_blocks - 1) / ((uint64_t)kWavesPerBlock * max_blocks);
-    const uint64_t want = (total + (uint64_t)kWavesPerBlock * per_wave - 1) / ((uint64_t)kWavesPerBlock * per_wave);
+    // Every workgroup should get the same number of chunks, or the launch
+    // ends with part of the grid idle: with at most max_blocks workgroups each
+    // takes ceil(total / max_blocks) chunks; use just enough workgroups.
+    const uint64_t per_block = (total + max_blocks - 1) / max_blocks;
+    const uint64_t want = (total + per_block - 1) / per_block;
     const unsigned grid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)max_blocks));
     hipLaunchKernelGGL(afx_decode_kernel, dim3(grid), dim3(kThreads), 0, stream, batch);
     return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
