@@ -56,22 +56,21 @@ struct TensorDesc {
     uint64_t n;
     uint64_t exp_words;
     uint64_t last_word4;   // highest 4-aligned word index w with w + 4 <= exp_words
-    uint64_t first_chunk;  // index of this tensor's chunk 0 in the launch
+    uint32_t n_chunks;     // ceil(n / 4096)
+    uint32_t blk_lo;       // workgroups [blk_lo, blk_hi) of the grid serve this tensor
+    uint32_t blk_hi;
+    uint32_t reserved;
 };
 
 struct Batch {
     TensorDesc t[AFX_MAX_JOBS_PER_LAUNCH];
     uint32_t n_tensors;
-    uint32_t reserved;
-    uint64_t total_chunks;
 };
 
 struct LutScratch {
-    uint32_t wave_count[kSymbolWaves][kMaxLen + 1];
-    uint32_t limit[kMaxLen + 1];  // end of each length's slice of the 12-bit index space
-    uint32_t first[kMaxLen + 1];  // first canonical code of each length
-    uint32_t start[kMaxLen + 1];  // position of that length's first symbol in `sorted`
-    uint8_t sorted[256];          // used symbols in (length, value) order
+    uint32_t wave_count[kSymbolWaves][kMaxLen + 1];  // symbols of each length per wave
+    uint32_t base[kMaxLen + 1];  // position in `sorted` of code 0 of each length, mod 2^32
+    uint8_t sorted[256];         // used symbols in (length, value) order
 };
 
 // Per-wave LDS: the chunk's code words while decoding, then its decoded
@@ -99,16 +98,15 @@ __device__ inline void wave_sync() {
 // starts the window. The length sits in the low bits so that a 32-bit shift
 // by the whole entry consumes exactly the code (the hardware reads only the
 // low 5 bits of a shift amount). All 1024 threads take part: thread s < 256
-// owns symbol s, then every thread s fills table entries [4 s, 4 s + 4).
-// Callers bracket it with barriers.
-__device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, LutScratch &S) {
+// owns symbol s and passes its code length (the others pass 0), then every
+// thread s fills table entries [4 s, 4 s + 4). Callers bracket it with
+// barriers.
+__device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1), wave = s / kWave;
-    uint32_t len = 0;
     uint32_t rank = 0;  // among same-length symbols of this wave with smaller value
+    if (len > kMaxLen) len = 0;  // only a corrupt blob gets here; treat as unused
     if (wave < kSymbolWaves) {
-        len = code_len[s];
-        if (len > kMaxLen) len = 0;  // only a corrupt blob gets here; treat as unused
 #pragma unroll
         for (uint32_t l = 1; l <= kMaxLen; ++l) {
             const uint64_t m = __ballot(len == l);
@@ -117,33 +115,49 @@ __device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, L
         }
     }
     __syncthreads();
-    if (s == 0) {
-        uint32_t code = 0, pos = 0;
-        for (uint32_t l = 1; l <= kMaxLen; ++l) {
-            uint32_t cnt = 0;
-            for (int w = 0; w < kSymbolWaves; ++w) cnt += S.wave_count[w][l];
-            S.first[l] = code;
-            S.start[l] = pos;
-            S.limit[l] = (code + cnt) << (kMaxLen - l);
-            pos += cnt;
-            code = (code + cnt) << 1;
+
+    // Every wave derives the canonical code in registers: lane l (1..12)
+    // holds the number of symbols of length l (cnt) and of them in waves
+    // before this one (below), the position of the first of them in
+    // (length, value) order (start), their first code (first) and the end of
+    // their slice of the 12-bit index space (limit).
+    const uint32_t ll = (uint32_t)lane;
+    uint32_t cnt = 0, below = 0;
+    if (ll >= 1 && ll <= kMaxLen) {
+#pragma unroll
+        for (int w = 0; w < kSymbolWaves; ++w) {
+            const uint32_t c = S.wave_count[w][ll];
+            cnt += c;
+            below += w < wave ? c : 0u;
         }
     }
-    __syncthreads();
-    if (len) {
-        uint32_t before = 0;
-        for (int w = 0; w < wave; ++w) before += S.wave_count[w][len];
-        S.sorted[(S.start[len] + before + rank) & 255] = (uint8_t)s;
+    uint32_t start = 0, first = 0;
+#pragma unroll
+    for (uint32_t m = 1; m < kMaxLen; ++m) {
+        const uint32_t cm = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)m);
+        if (m < ll) {
+            start += cm;
+            first += cm << (ll - m);  // first[l] = (first[l-1] + cnt[l-1]) << 1, unrolled
+        }
     }
+    const uint32_t limit = (first + cnt) << (kMaxLen - (ll <= kMaxLen ? ll : kMaxLen));
+    // (all lanes active: a lane reads another lane's register)
+    const uint32_t pos = (uint32_t)__shfl((int)start, (int)len) + (uint32_t)__shfl((int)below, (int)len) + rank;
+    if (len) S.sorted[pos & 255] = (uint8_t)s;
+    if (wave == 0 && ll >= 1 && ll <= kMaxLen) S.base[ll] = start - first;
     __syncthreads();
 
     // An entry's length is one more than the number of length slices that
     // end at or before it; its symbol follows from the code's distance to
     // that length's first code.
+    uint32_t lim[kMaxLen];
+#pragma unroll
+    for (uint32_t q = 1; q < kMaxLen; ++q) lim[q] = (uint32_t)__builtin_amdgcn_readlane((int)limit, (int)q);
     auto entry = [&](uint32_t idx) -> uint32_t {
         uint32_t l = 1;
-        for (uint32_t k = 1; k < kMaxLen; ++k) l += idx >= S.limit[k] ? 1u : 0u;
-        const uint32_t j = S.start[l] + ((idx >> (kMaxLen - l)) - S.first[l]);
+#pragma unroll
+        for (uint32_t q = 1; q < kMaxLen; ++q) l += idx >= lim[q] ? 1u : 0u;
+        const uint32_t j = S.base[l] + (idx >> (kMaxLen - l));
         return ((uint32_t)S.sorted[j & 255] << 8) | l;
     };
     constexpr uint32_t kPer = kLutEntries / kThreads;  // 4 entries per thread
@@ -154,7 +168,6 @@ __device__ void build_lut(const uint8_t *__restrict__ code_len, uint16_t *lut, L
         const uint32_t d = e0 | (e0 << 16);
         *reinterpret_cast<uint2 *>(lut + i0) = make_uint2(d, d);
     } else {
-#pragma unroll
         for (uint32_t j = 0; j < kPer; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
     }
 }
@@ -300,26 +313,6 @@ __device__ inline void store_out(uint16_t *p, uint4 v) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
 }
 
-__device__ inline uint64_t chunks_of(const TensorDesc &T) { return (T.n + kChunk - 1) / kChunk; }
-
-// The grid is split among the tensors in proportion to their chunk counts,
-// so that a workgroup serves about one tensor (one decode table to build); a
-// tensor too small for a workgroup of its own is served by the workgroup at
-// its position. Within a tensor the chunks go round its workgroups (the k-th
-// of nb takes chunks k, k + nb, k + 2 nb, ...), so that at any moment each
-// array is streamed in one narrow band. Blocks [lo, hi) serve tensor t.
-__device__ inline bool block_share(const Batch &B, uint32_t t, uint64_t b, uint64_t &k, uint64_t &nb) {
-    const uint64_t grid = gridDim.x, total = B.total_chunks;
-    const uint64_t p0 = B.t[t].first_chunk, p1 = p0 + chunks_of(B.t[t]);
-    const uint64_t lo = grid * p0 / total;
-    uint64_t hi = grid * p1 / total;
-    if (hi <= lo) hi = lo + 1;
-    if (b < lo || b >= hi) return false;
-    k = b - lo;
-    nb = hi - lo;
-    return true;
-}
-
 // Restore one chunk: decode the staged code words, merge with the
 // sign/mantissa bytes, store. `stage` holds the chunk's code words on entry
 // and is free (but for the exponent bytes just written) on exit.
@@ -413,38 +406,43 @@ void afx_decode_kernel(const Batch batch) {
 
     for (uint32_t t = 0; t < batch.n_tensors; ++t) {
         const TensorDesc &T = batch.t[t];
-        uint64_t k, nb;
-        if (!block_share(batch, t, b, k, nb) || k >= chunks_of(T)) continue;
-        // The workgroup's chunks of T, j = 0, 1, ...: chunk k + j nb. Wave w
-        // starts with j = w and j = w + 16; after that each wave claims the
-        // next unclaimed j when it starts a chunk, so waves that the SIMDs
-        // serve faster restore more chunks and all finish together.
-        const uint64_t mine = (chunks_of(T) - k + nb - 1) / nb;
-        uint64_t jc = wave, jn = wave + kWavesPerBlock;
+        // Workgroups [blk_lo, blk_hi) serve T (the host splits the grid among
+        // the tensors in proportion to their chunk counts). Within a tensor the
+        // chunks go round its workgroups, so that all of them move through each
+        // array together, in one narrow band: the k-th of nb takes chunks
+        // k + j nb, j = 0, 1, ... Wave w starts with j = w and j = w + 16;
+        // after that each wave claims the next unclaimed j when it starts a
+        // chunk, so waves that the SIMDs serve faster restore more chunks and
+        // all finish together.
+        if (b < T.blk_lo || b >= T.blk_hi) continue;
+        const uint32_t k = (uint32_t)b - T.blk_lo, nb = T.blk_hi - T.blk_lo;
+        if (k >= T.n_chunks) continue;
+        const uint32_t mine = (T.n_chunks - k + nb - 1) / nb;
+        uint32_t jc = wave, jn = wave + kWavesPerBlock;
         const bool has_c = jc < mine;
         bool has_n = jn < mine;
-        // start fetching the first two chunks' bases and the first one's
-        // gaps; building the decode table hides these loads
+        // Fetch the code lengths, the first two chunks' bases and the first
+        // one's gaps, then the first chunk's code words; building the decode
+        // table hides the second round trip.
+        const uint32_t len = wave < kSymbolWaves ? T.code_len[threadIdx.x] : 0;
         uint64_t bases_c = 0, bases_n = 0;
         Gaps gaps{0, 0};
+        if (has_c) bases_c = load_bases(T, k + (uint64_t)jc * nb, lane);
+        if (has_n) bases_n = load_bases(T, k + (uint64_t)jn * nb, lane);
+        if (has_c) gaps = load_gaps(T, k + (uint64_t)jc * nb, lane);
+        ChunkGeom g{};
+        StreamRegs s;
         if (has_c) {
-            bases_c = load_bases(T, k + jc * nb, lane);
-            gaps = load_gaps(T, k + jc * nb, lane);
+            g = geom_from_lanes(bases_c);
+            load_stream(T, g, lane, s);
         }
-        if (has_n) bases_n = load_bases(T, k + jn * nb, lane);
         __syncthreads();  // every wave is done with the previous table and counter
         if (threadIdx.x == 0) next_j = 2 * kWavesPerBlock;
-        build_lut(T.code_len, lut, scratch);  // ends with a barrier
+        build_lut(len, lut, scratch);  // ends with a barrier
         __syncthreads();
         if (!has_c) continue;
-
-        ChunkGeom g = geom_from_lanes(bases_c);
-        {
-            StreamRegs s;
-            load_stream(T, g, lane, s);
-            put_stream(T, g, s, my_stage, lane);
-            wave_sync();
-        }
+        put_stream(T, g, s, my_stage, lane);
+        wave_sync();
         ChunkGeom gn = geom_from_lanes(bases_n);
         while (true) {
             // recompute per-lane offsets every chunk instead of keeping them
@@ -452,7 +450,7 @@ void afx_decode_kernel(const Batch batch) {
             asm volatile("" : "+v"(lane));
             // While chunk jc decodes, fetch the code words and gaps of jn,
             // claim the chunk after it and fetch that one's bases.
-            uint64_t jnn = ~(uint64_t)0;
+            uint32_t jnn = ~0u;
             bool has_nn = false;
             StreamRegs sn;
             Gaps gaps_n{0, 0};
@@ -463,11 +461,11 @@ void afx_decode_kernel(const Batch batch) {
                 jnn = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
                 has_nn = jnn < mine;
                 load_stream(T, gn, lane, sn);
-                gaps_n = load_gaps(T, k + jn * nb, lane);
-                if (has_nn) bases_nn = load_bases(T, k + jnn * nb, lane);
+                gaps_n = load_gaps(T, k + (uint64_t)jn * nb, lane);
+                if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
             }
             ChunkGeom gnn;
-            restore_chunk(T, k + jc * nb, g, gaps, lut, my_stage, lane, bases_nn, gnn);
+            restore_chunk(T, k + (uint64_t)jc * nb, g, gaps, lut, my_stage, lane, bases_nn, gnn);
             if (!has_n) break;
             wave_sync();  // the exponent bytes have been read
             put_stream(T, gn, sn, my_stage, lane);
@@ -519,7 +517,7 @@ int check_job(const afx_job &j) {
     return AFX_OK;
 }
 
-TensorDesc describe(const afx_job &j, uint64_t first_chunk) {
+TensorDesc describe(const afx_job &j) {
     const afx_info &I = *j.info;
     const uint8_t *b = static_cast<const uint8_t *>(j.blob_dev);
     TensorDesc d;
@@ -532,7 +530,9 @@ TensorDesc describe(const afx_job &j, uint64_t first_chunk) {
     d.n = I.n_elems;
     d.exp_words = I.exp_words;
     d.last_word4 = (I.exp_words - 4) & ~(uint64_t)3;  // exp_words >= 4: the stream ends with 4 zero words
-    d.first_chunk = first_chunk;
+    d.n_chunks = (uint32_t)I.n_chunks;  // n <= 2^40 elements: fewer than 2^28 chunks
+    d.blk_lo = d.blk_hi = 0;
+    d.reserved = 0;
     return d;
 }
 
@@ -540,14 +540,14 @@ TensorDesc describe(const afx_job &j, uint64_t first_chunk) {
 int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
     Batch batch;
     batch.n_tensors = 0;
-    batch.reserved = 0;
     uint64_t total = 0;
+    uint64_t first[AFX_MAX_JOBS_PER_LAUNCH];
     for (size_t i = 0; i < n_jobs; ++i) {
         if (jobs[i].info->n_elems == 0) continue;
-        batch.t[batch.n_tensors++] = describe(jobs[i], total);
+        first[batch.n_tensors] = total;
+        batch.t[batch.n_tensors++] = describe(jobs[i]);
         total += jobs[i].info->n_chunks;
     }
-    batch.total_chunks = total;
     if (total == 0) return AFX_OK;
     int max_blocks = 0;
     int rc = max_blocks_for_current_device(&max_blocks);
@@ -557,8 +557,18 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
     // takes ceil(total / max_blocks) chunks; use just enough workgroups.
     const uint64_t per_block = (total + max_blocks - 1) / max_blocks;
     const uint64_t want = (total + per_block - 1) / per_block;
-    const unsigned grid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)max_blocks));
-    hipLaunchKernelGGL(afx_decode_kernel, dim3(grid), dim3(kThreads), 0, stream, batch);
+    const uint64_t grid = std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)max_blocks));
+    // Split the grid among the tensors in proportion to their chunk counts;
+    // a tensor too small for a workgroup of its own is served by the
+    // workgroup at its position (which may serve a neighbour too).
+    for (uint32_t t = 0; t < batch.n_tensors; ++t) {
+        const uint64_t lo = grid * first[t] / total;
+        uint64_t hi = grid * (first[t] + batch.t[t].n_chunks) / total;
+        if (hi <= lo) hi = lo + 1;
+        batch.t[t].blk_lo = (uint32_t)lo;
+        batch.t[t].blk_hi = (uint32_t)hi;
+    }
+    hipLaunchKernelGGL(afx_decode_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, batch);
     return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
 }
 
