@@ -172,34 +172,47 @@ def check_unit(u: Unit, out) -> bool:
     return ok
 
 
-def resident_decode_ms(units, steps: int = 3, device="cuda") -> float:
-    """Restore every unit back to back with all compressed bytes already in
-    HBM (two alternating output buffers); milliseconds per whole-model pass."""
+def resident_decode(units, steps: int = 3, device="cuda", check: bool = False) -> dict:
+    """Restore the whole model with every unit's compressed bytes already in
+    HBM, into one output region per unit (the restored model, ~29.5 GB, and
+    the compressed one, ~20.5 GB, both fit in HBM): one afx_decode_layer_async
+    call per unit, back to back on one stream. (Packing several layers into
+    each 32-tensor launch is slower: mid-sized tensors then get too few or too
+    many whole workgroups.) Returns milliseconds per whole-model pass and, with
+    ``check``, whether every unit came back bit-exact (needs the raw bits)."""
     import torch
 
     dev = torch.device(device)
     blobs = [u.host[:u.blob_bytes].to(dev) for u in units]
-    max_vals = max(sum(_out_slot(int(i.n_elems)) for i in u.infos) for u in units)
-    outs = [torch.empty(max_vals, dtype=torch.int16, device=dev) for _ in range(2)]
-    jobs = []
+    slots = [sum(_out_slot(int(i.n_elems)) for i in u.infos) for u in units]
+    out = torch.empty(sum(slots), dtype=torch.int16, device=dev)
+    calls, base = [], 0
     for k, u in enumerate(units):
-        oo, js = 0, []
+        oo, jobs = base, []
         for info, off in zip(u.infos, u.offsets):
             n = int(info.n_elems)
-            js.append((info, blobs[k].data_ptr() + off, outs[k % 2].data_ptr() + 2 * oo, 2 * n))
+            jobs.append((info, blobs[k].data_ptr() + off, out.data_ptr() + 2 * oo, 2 * n))
             oo += _out_slot(n)
-        jobs.append(afx.make_jobs(js))
+        base += slots[k]
+        calls.append(afx.make_jobs(jobs))
     s = torch.cuda.current_stream(dev)
-    for j in jobs:  # warm-up pass
-        afx.afx_decode_layer_async(j, s.cuda_stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for arr in calls:  # warm-up pass (also the checked one)
+        afx.afx_decode_layer_async(arr, s.cuda_stream)
     torch.cuda.synchronize(dev)
+    exact = None
+    if check:
+        exact, base = True, 0
+        for k, u in enumerate(units):
+            exact &= check_unit(u, out[base:base + slots[k]])
+            base += slots[k]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for _ in range(steps):
-        for j in jobs:
-            afx.afx_decode_layer_async(j, s.cuda_stream)
+        for arr in calls:
+            afx.afx_decode_layer_async(arr, s.cuda_stream)
     e1.record(s)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
-    del blobs, outs
-    return ms
+    del blobs, out
+    launches = sum((len(a) + afx.MAX_JOBS_PER_LAUNCH - 1) // afx.MAX_JOBS_PER_LAUNCH for a in calls)
+    return {"ms": ms, "launches": launches, "bit_exact": exact}

@@ -220,3 +220,23 @@ def test_streamed_units_double_buffered():
     assert stream.check_unit(units[-1], st.out[(len(units) - 1) % 2])
     assert stream.check_unit(units[-2], st.out[(len(units) - 2) % 2])
     assert res["e2e_ms"] > 0 and len(res["decode_ms"]) == len(units)
+
+
+def test_resident_model_one_launch_per_unit():
+    """Every unit's compressed bytes resident in HBM, one call per unit back
+    to back, each unit into its own output region; every unit bit-exact."""
+    from lossless_bf16_weight_afx_amd import stream
+
+    T = synth.TensorSpec
+    rng = np.random.default_rng(21)
+    units_specs = []
+    for u in range(12):
+        units_specs.append([T(f"m{u}.a", (int(rng.integers(1, 700)), 512), "normal", 600 + 3 * u),
+                            T(f"m{u}.b", (int(rng.integers(1, 9000)),), "t4", 601 + 3 * u),
+                            T(f"m{u}.n", (128,), "normal", 602 + 3 * u, 1.0, 0.05)])
+    say("[gpu] case resident model: build store (36 tensors)")
+    units = stream.build_model(units_specs, threads=8, keep_raw=True)
+    res = stream.resident_decode(units, steps=2, check=True)
+    assert res["launches"] == 12
+    assert res["bit_exact"] is True
+    assert res["ms"] > 0
