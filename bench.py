@@ -8,7 +8,9 @@ afx_decode_layer_async call (one kernel launch for up to 32 tensors).
 Default workload: one Qwen3-14B-shaped decoder layer (11 tensors, 330.3M
 BF16 values, 0.66 GB restored), the unit the time-to-ready model of "Why
 Weight Offloading Slows Inference" reasons about. Other workloads:
-tensor-1024 (1024x1024), q_proj (5120x5120), embedding (151936x5120).
+tensor-1024 (1024x1024), q_proj (5120x5120), embedding (151936x5120), model
+(the whole 40-layer model, compressed in pinned host memory) and disk (the
+whole model stored compressed in a file, read cold, copied and restored).
 
 Prints one JSON line with the throughput of restored BF16, the HBM roofline
 fraction of the decode kernel (hipEvent timing on the launch stream), and the
@@ -95,8 +97,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer", choices=["layer", "tensor-1024", "q_proj", "embedding", "model"])
-    ap.add_argument("--layers", type=int, default=40, help="decoder layers of the streamed model (--workload model)")
+    ap.add_argument("--workload", default="layer",
+                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk"])
+    ap.add_argument("--layers", type=int, default=40,
+                    help="decoder layers of the whole model (--workload model or disk)")
+    ap.add_argument("--store-dir", default=os.environ.get("TMPDIR") or "/tmp",
+                    help="directory for the model store file (--workload disk)")
+    ap.add_argument("--keep-store", action="store_true", help="keep the store file afterwards (--workload disk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0,
                     help="rotate over this many blob/output copies (default: enough for about 4 GB between "
@@ -120,6 +127,8 @@ def main() -> int:
     threads = min(16, host_threads())
     if args.workload == "model":
         return bench_model(args, threads)
+    if args.workload == "disk":
+        return bench_disk(args, threads)
     workload, specs = workload_specs(args.workload)
 
     # ---- inputs: generate, encode with the library's encoder, move to HBM
@@ -311,6 +320,80 @@ def bench_model(args, threads: int) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0 if exact else 1
+
+
+def bench_disk(args, threads: int) -> int:
+    """The whole synthetic model stored compressed in a file and made ready
+    in HBM: read from disk (O_DIRECT, so the page cache never serves it) into
+    pinned memory, copied to the GPU, restored; the three steps of
+    consecutive units overlap. `value` is restored BF16 bytes per second of
+    the whole pass (time to ready weights); the read, copy and restore rates
+    measured alone are reported beside it, with the pages' Eq. (1) and
+    Eq. (2) evaluated on them."""
+    import torch
+
+    from lossless_bf16_weight_afx_amd import store, synth
+
+    specs = synth.model_units(args.layers)
+    path = os.path.join(args.store_dir, f"afx_model_{args.layers}l_{os.getpid()}.afxs")
+    t0 = time.time()
+    st = store.write_store(path, specs, threads=threads, progress=log)
+    write_s = time.time() - t0
+    try:
+        try:
+            fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+            os.close(fd)
+            direct = True
+        except OSError:
+            direct = False
+        log(f"[bench] store {path}: {st.file_bytes} B written in {write_s:.0f}s; O_DIRECT={direct}")
+        ds = store.DiskStreamer(st, threads=threads, direct=direct)
+        stored = sum(u.bytes for u in st.units)
+        restored = st.restored_bytes
+        # bit-exact pass: the embedding, the first and last layers, the head
+        check_idx = {0, 1, len(st.units) - 2, len(st.units) - 1}
+        ok = []
+        ds.run(on_unit=lambda i, u, out: ok.append(store.check_unit(out, specs[i])) if i in check_idx else None)
+        exact = len(ok) == len(check_idx) and all(ok)
+        log(f"[bench] checked pass over {sorted(check_idx)}: bit_exact={exact}")
+        read_s = float(np.median([ds.read_only_s() for _ in range(max(1, min(args.steps, 3)))]))
+        copy_s = float(np.median([ds.copy_only_s() for _ in range(3)]))
+        runs = [ds.run() for _ in range(max(1, args.steps))]
+        e2e_s = float(np.median([r["e2e_s"] for r in runs]))
+        dec_ms = float(np.median([sum(r["decode_ms"]) for r in runs]))
+        b_disk = stored / read_s
+        b_link = stored / copy_s
+        layer = st.units[1]
+        s_disk, s_full = layer.bytes, 2 * layer.n_values
+        t_unpack = float(np.median([r["decode_ms"][1] for r in runs])) * 1e-3
+        eq1 = {"read_s": round(s_disk / b_disk, 5), "copy_s": round(s_disk / b_link, 5), "unpack_s": round(t_unpack, 6),
+               "t_prep_serial_s": round(s_disk / b_disk + s_disk / b_link + t_unpack, 5),
+               "uncompressed_read_s": round(s_full / b_disk, 5)}
+        eq2 = {"saved_read_s": round((s_full - s_disk) / b_disk, 5), "unpack_s": round(t_unpack, 6),
+               "compression_pays": bool((s_full - s_disk) / b_disk > t_unpack)}
+        line = {
+            "metric": "ready BF16 weights GB/s from disk on 1 MI355X (read + copy + restore, overlapped)",
+            "value": round(restored / e2e_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": 0, "ms_per_step": round(e2e_s * 1e3, 1), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+            "config": {"workload": f"qwen3-14b-model-{args.layers}-layers-from-disk", "units": len(st.units),
+                       "restored_bytes": restored, "stored_bytes": stored, "o_direct": direct,
+                       "reader_threads": threads},
+            "bit_exact": bool(exact),
+            "disk_read_GBps": round(b_disk / 1e9, 3), "link_GBps": round(b_link / 1e9, 2),
+            "decode_only_GBps": round(restored / (dec_ms * 1e-3) / 1e9, 1),
+            "uncompressed_read_equiv_s": round(restored / b_disk, 2), "pass_s": round(e2e_s, 2),
+            "read_bound_s": round(stored / b_disk, 2),
+            "eq1_per_layer": eq1, "eq2_per_layer": eq2, "store_write_s": round(write_s, 1),
+            "roofline": None, "cpu_baseline": None,
+        }
+        print(json.dumps(line), flush=True)
+        del ds
+        torch.cuda.empty_cache()
+        return 0 if exact else 1
+    finally:
+        if not args.keep_store:
+            os.unlink(path)
 
 
 if __name__ == "__main__":

@@ -59,7 +59,8 @@ typedef enum afx_status {
     AFX_E_BUFFER_TOO_SMALL = -5,/* blob shorter than its header says, or output too small */
     AFX_E_MISALIGNED = -6,      /* device pointer not 16-byte aligned */
     AFX_E_HIP = -7,             /* a HIP runtime call failed (launch or execution) */
-    AFX_E_UNSUPPORTED = -8      /* request beyond what this build supports */
+    AFX_E_UNSUPPORTED = -8,     /* request beyond what this build supports */
+    AFX_E_IO = -9               /* a file could not be opened or read in full */
 } afx_status;
 
 /* What afx_query reports about a blob. Offsets are in bytes from the blob's
@@ -141,6 +142,26 @@ int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len
 int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape,
                const uint8_t code_len[256], uint64_t total_bits, void *blob, size_t blob_bytes,
                int threads);
+
+/* ---- Storage (host). "Why Weight Offloading Slows Inference" (section
+ * "The path from storage to the GPU", Figure 1, and Eq. (1)) reads a stored
+ * weight from the SSD into RAM before unpacking it and copying it to the GPU;
+ * the page measures that read with the page cache cleared. */
+
+#define AFX_READ_DIRECT 1u /* open with O_DIRECT: bypass the page cache */
+
+/* afx_file_read: read bytes [offset, offset + bytes) of the file at path into
+ * dst (host memory owned by the caller, any alignment; pinned memory lets a
+ * following copy to the GPU start from it), with `threads` workers (<= 0:
+ * the hardware thread count) each issuing 4 MiB preads. With
+ * AFX_READ_DIRECT each worker reads the enclosing 4096-aligned range into
+ * its own page-aligned 4 MiB buffer and copies the requested part to dst
+ * (the kernel refuses direct transfers into GPU-pinned host memory). On
+ * error dst may be partly written.
+ * Errors: AFX_E_INVALID_ARG (NULL path or dst, unknown flag),
+ * AFX_E_UNSUPPORTED (the file system refuses O_DIRECT), AFX_E_IO (open or
+ * read failed, or the file ends inside the range). */
+int afx_file_read(const char *path, uint64_t offset, uint64_t bytes, void *dst, int threads, unsigned flags);
 
 #ifdef __cplusplus
 }

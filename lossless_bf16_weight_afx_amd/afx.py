@@ -22,11 +22,13 @@ AFX_E_BUFFER_TOO_SMALL = -5
 AFX_E_MISALIGNED = -6
 AFX_E_HIP = -7
 AFX_E_UNSUPPORTED = -8
+AFX_E_IO = -9
 MAX_JOBS_PER_LAUNCH = 32
+AFX_READ_DIRECT = 1
 
 # Every symbol include/afx.h declares.
 EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_status_str",
-           "afx_encode_plan", "afx_encode")
+           "afx_encode_plan", "afx_encode", "afx_file_read")
 
 
 class AfxError(RuntimeError):
@@ -97,6 +99,9 @@ def lib() -> ctypes.CDLL:
         L.afx_encode.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint32, u64p, u8p, ctypes.c_uint64,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
         L.afx_encode.restype = ctypes.c_int
+        L.afx_file_read.argtypes = [ctypes.c_char_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_uint]
+        L.afx_file_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -191,6 +196,12 @@ def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None, plan=None)
                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), bits, ctypes.c_void_p(addr),
                             cap, threads), "afx_encode")
     return out[:nbytes] if isinstance(out, np.ndarray) else nbytes
+
+
+def afx_file_read(path: str, offset: int, nbytes: int, dst: int, threads: int = 0, direct: bool = True) -> None:
+    """Read nbytes at offset of the file into host memory at address dst."""
+    _check(lib().afx_file_read(os.fsencode(path), offset, nbytes, ctypes.c_void_p(dst), threads,
+                               AFX_READ_DIRECT if direct else 0), "afx_file_read")
 
 
 # ---------------------------------------------------------------------------

@@ -289,6 +289,7 @@ const char *afx_status_str(int status) {
         case AFX_E_MISALIGNED: return "device pointer not 16-byte aligned";
         case AFX_E_HIP: return "HIP runtime error";
         case AFX_E_UNSUPPORTED: return "unsupported request";
+        case AFX_E_IO: return "file could not be opened or read in full";
         default: return "unknown status";
     }
 }

@@ -4,6 +4,7 @@ Blobs come from the oracle's encoder; the expected values are the generated
 inputs themselves, which the oracle decoder reproduces bit for bit (pinned in
 test_oracle_pins.py). Every comparison is exact (integer bit patterns).
 """
+import os
 import sys
 
 import numpy as np
@@ -240,3 +241,41 @@ def test_resident_model_one_launch_per_unit():
     assert res["launches"] == 12
     assert res["bit_exact"] is True
     assert res["ms"] > 0
+
+
+def test_disk_store_read_copy_restore(tmp_path):
+    """Units read from a store file (O_DIRECT where the file system allows it)
+    into pinned memory, copied and restored with the three steps overlapped;
+    every unit bit-exact, staging and device buffers reused."""
+    from lossless_bf16_weight_afx_amd import store
+
+    T = synth.TensorSpec
+    units_specs = [
+        [T("d0.w", (1500, 640), "normal", 41), T("d0.norm", (5120,), "normal", 42, 1.0, 0.05)],
+        [T("d1.w", (512, 4096), "t4", 43)],
+        [T("d2.a", (77, 33), "normal", 44), T("d2.b", (4097,), "normal", 45)],
+        [T("d3.w", (2000, 1000), "normal", 46)],
+        [T("d4.w", (33, 4096), "t4", 47), T("d4.n", (128,), "normal", 48, 1.0, 0.05)],
+        [T("d5.w", (4096, 700), "normal", 49)],
+    ]
+    path = str(tmp_path / "model.afxs")
+    say("[gpu] case disk store: write")
+    st = store.write_store(path, units_specs, threads=8)
+    try:
+        fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+        os.close(fd)
+        direct = True
+    except OSError:
+        direct = False
+    ds = store.DiskStreamer(st, threads=4, direct=direct)
+    ok = []
+    say(f"[gpu] case disk store: checked pass (direct={direct})")
+    ds.run(on_unit=lambda i, u, out: ok.append(store.check_unit(out, units_specs[i])))
+    assert ok == [True] * len(units_specs)
+    say("[gpu] case disk store: free-running pass")
+    res = ds.run()
+    torch.cuda.synchronize()
+    n = len(units_specs)
+    assert store.check_unit(ds.out[(n - 1) % 2], units_specs[-1])
+    assert store.check_unit(ds.out[(n - 2) % 2], units_specs[-2])
+    assert res["e2e_s"] > 0 and len(res["decode_ms"]) == n
