@@ -143,6 +143,20 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
                const uint8_t code_len[256], uint64_t total_bits, void *blob, size_t blob_bytes,
                int threads);
 
+/* ---- Unpack on the host. "Why Weight Offloading Slows Inference" (section
+ * "The path from storage to the GPU", Figure 1) unpacks a compressed weight
+ * in RAM between the read and the copy to the GPU, and section "Lossless
+ * compression" finds that placement too slow for compression to pay
+ * (Eq. (2)). The GPU entry points above never call this; it exists to
+ * measure that placement beside the GPU restore. */
+
+/* afx_decode_host: validate a host blob as afx_query does, then restore its
+ * n_elems BF16 bit patterns into out (host memory, out_bytes >= 2 n), with
+ * `threads` workers over chunks (<= 0: hardware thread count).
+ * Errors: as afx_query; AFX_E_INVALID_ARG (NULL out with n > 0),
+ * AFX_E_BUFFER_TOO_SMALL (out_bytes < 2 n). */
+int afx_decode_host(const void *blob_host, size_t blob_bytes, uint16_t *out, size_t out_bytes, int threads);
+
 /* ---- Storage (host). "Why Weight Offloading Slows Inference" (section
  * "The path from storage to the GPU", Figure 1, and Eq. (1)) reads a stored
  * weight from the SSD into RAM before unpacking it and copying it to the GPU;

@@ -28,7 +28,7 @@ AFX_READ_DIRECT = 1
 
 # Every symbol include/afx.h declares.
 EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_status_str",
-           "afx_encode_plan", "afx_encode", "afx_file_read")
+           "afx_encode_plan", "afx_encode", "afx_file_read", "afx_decode_host")
 
 
 class AfxError(RuntimeError):
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.afx_file_read.argtypes = [ctypes.c_char_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_uint]
         L.afx_file_read.restype = ctypes.c_int
+        L.afx_decode_host.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        L.afx_decode_host.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -196,6 +198,28 @@ def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None, plan=None)
                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), bits, ctypes.c_void_p(addr),
                             cap, threads), "afx_encode")
     return out[:nbytes] if isinstance(out, np.ndarray) else nbytes
+
+
+def afx_decode_host(blob, blob_bytes: int | None = None, out=None, threads: int = 0):
+    """Restore a host blob on the host (the pages' placement of the unpack).
+
+    ``blob`` is a numpy uint8 array or an address (with blob_bytes); ``out``
+    a numpy uint16 array, an (address, capacity) pair, or None (allocated).
+    Returns the uint16 array, or None when out is an address pair."""
+    if isinstance(blob, np.ndarray):
+        assert blob.dtype == np.uint8 and blob.flags.c_contiguous
+        addr, size = blob.ctypes.data, blob.size if blob_bytes is None else blob_bytes
+    else:
+        addr, size = int(blob), int(blob_bytes)
+    if out is None:
+        out = np.empty(int(afx_query(addr, size).n_elems), np.uint16)
+    if isinstance(out, np.ndarray):
+        assert out.dtype == np.uint16 and out.flags.c_contiguous
+        oaddr, cap = out.ctypes.data, 2 * out.size
+    else:
+        oaddr, cap = int(out[0]), int(out[1])
+    _check(lib().afx_decode_host(ctypes.c_void_p(addr), size, ctypes.c_void_p(oaddr), cap, threads), "afx_decode_host")
+    return out if isinstance(out, np.ndarray) else None
 
 
 def afx_file_read(path: str, offset: int, nbytes: int, dst: int, threads: int = 0, direct: bool = True) -> None:

@@ -273,6 +273,97 @@ class DiskStreamer:
         return time.perf_counter() - t0
 
 
+class HostUnpackStreamer:
+    """The pages' placement of the unpack, for comparison: read each unit
+    from disk into pinned memory (reader thread, two units ahead), restore it
+    on the host into a pinned BF16 buffer with afx_decode_host, and copy the
+    restored bytes (S, not S_disk) to the GPU on a side stream while the next
+    unit is being restored."""
+
+    N_HOST = 3  # pinned staging buffers for stored bytes
+    N_OUT = 2  # pinned BF16 buffers and device outputs
+
+    def __init__(self, store: Store, device="cuda", read_threads: int = 16, unpack_threads: int = 16,
+                 direct: bool = True):
+        import torch
+
+        self.torch = torch
+        self.store = store
+        self.dev = torch.device(device)
+        self.read_threads = read_threads
+        self.unpack_threads = unpack_threads
+        self.direct = direct
+        max_unit = max(u.bytes for u in store.units)
+        max_vals = max(sum(_out_slot(int(np.prod(t.shape))) for t in u.tensors) for u in store.units)
+        self.host = [torch.empty(max_unit, dtype=torch.uint8, pin_memory=True) for _ in range(self.N_HOST)]
+        self.host_out = [torch.empty(max_vals, dtype=torch.int16, pin_memory=True) for _ in range(self.N_OUT)]
+        self.out = [torch.empty(max_vals, dtype=torch.int16, device=self.dev) for _ in range(self.N_OUT)]
+        self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
+
+    def run(self, on_unit=None) -> dict:
+        """One pass; ``on_unit(i, unit, out_tensor)`` runs after unit i is on
+        the GPU (it synchronizes; use only off the clock)."""
+        torch = self.torch
+        units = self.store.units
+        n = len(units)
+        copied = [torch.cuda.Event() for _ in range(n)]
+        reader = ThreadPoolExecutor(max_workers=1)
+
+        def read(i):
+            u, h = units[i], i % self.N_HOST
+            t0 = time.perf_counter()
+            afx.afx_file_read(self.store.path, u.offset, u.bytes, self.host[h].data_ptr(), self.read_threads,
+                              self.direct)
+            return time.perf_counter() - t0
+
+        torch.cuda.synchronize(self.dev)
+        t_start = time.perf_counter()
+        futs = {i: reader.submit(read, i) for i in range(min(self.N_HOST, n))}
+        read_s = unpack_s = wait_s = 0.0
+        try:
+            for i, u in enumerate(units):
+                tw = time.perf_counter()
+                read_s += futs.pop(i).result()
+                wait_s += time.perf_counter() - tw
+                h, o = i % self.N_HOST, i % self.N_OUT
+                if i >= self.N_OUT:
+                    copied[i - self.N_OUT].synchronize()  # its pinned BF16 buffer has been copied out
+                t0 = time.perf_counter()
+                oo = 0
+                for t in u.tensors:
+                    m = int(np.prod(t.shape))
+                    afx.afx_decode_host(self.host[h].data_ptr() + t.offset, t.bytes,
+                                        (self.host_out[o].data_ptr() + 2 * oo, 2 * m), self.unpack_threads)
+                    oo += _out_slot(m)
+                unpack_s += time.perf_counter() - t0
+                if i + self.N_HOST < n:  # staging buffer h is free again
+                    futs[i + self.N_HOST] = reader.submit(read, i + self.N_HOST)
+                with torch.cuda.stream(self.copy_stream):
+                    self.out[o][:oo].copy_(self.host_out[o][:oo], non_blocking=True)
+                    copied[i].record(self.copy_stream)
+                if on_unit is not None:
+                    copied[i].synchronize()
+                    on_unit(i, u, self.out[o])
+            torch.cuda.synchronize(self.dev)
+        finally:
+            reader.shutdown(wait=True)
+        return {"e2e_s": time.perf_counter() - t_start, "read_s": read_s, "unpack_s": unpack_s, "wait_s": wait_s,
+                "restored_bytes": self.store.restored_bytes}
+
+    def unpack_only_s(self, i: int) -> float:
+        """Time the host restore of unit i alone (its bytes read first)."""
+        u = self.store.units[i]
+        afx.afx_file_read(self.store.path, u.offset, u.bytes, self.host[0].data_ptr(), self.read_threads, self.direct)
+        t0 = time.perf_counter()
+        oo = 0
+        for t in u.tensors:
+            m = int(np.prod(t.shape))
+            afx.afx_decode_host(self.host[0].data_ptr() + t.offset, t.bytes,
+                                (self.host_out[0].data_ptr() + 2 * oo, 2 * m), self.unpack_threads)
+            oo += _out_slot(m)
+        return time.perf_counter() - t0
+
+
 def check_unit(out, specs) -> bool:
     """Regenerate a unit's original bits and compare with its restore."""
     import torch

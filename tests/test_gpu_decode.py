@@ -279,3 +279,10 @@ def test_disk_store_read_copy_restore(tmp_path):
     assert store.check_unit(ds.out[(n - 1) % 2], units_specs[-1])
     assert store.check_unit(ds.out[(n - 2) % 2], units_specs[-2])
     assert res["e2e_s"] > 0 and len(res["decode_ms"]) == n
+    del ds
+    # the pages' placement: unpack on the host, copy the restored bytes
+    hs = store.HostUnpackStreamer(st, read_threads=4, unpack_threads=4, direct=direct)
+    ok = []
+    say("[gpu] case disk store: host-unpack pass")
+    hs.run(on_unit=lambda i, u, out: ok.append(store.check_unit(out, units_specs[i])))
+    assert ok == [True] * len(units_specs)
