@@ -98,7 +98,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk"])
+                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk", "tiers"])
     ap.add_argument("--layers", type=int, default=40,
                     help="decoder layers of the whole model (--workload model or disk)")
     ap.add_argument("--store-dir", default=os.environ.get("TMPDIR") or "/tmp",
@@ -129,6 +129,8 @@ def main() -> int:
         return bench_model(args, threads)
     if args.workload == "disk":
         return bench_disk(args, threads)
+    if args.workload == "tiers":
+        return bench_tiers(args, threads)
     workload, specs = workload_specs(args.workload)
 
     # ---- inputs: generate, encode with the library's encoder, move to HBM
@@ -410,6 +412,77 @@ def bench_disk(args, threads: int) -> int:
         del hs
         torch.cuda.empty_cache()
         return 0 if line["bit_exact"] else 1
+    finally:
+        if not args.keep_store:
+            os.unlink(path)
+
+
+def bench_tiers(args, threads: int) -> int:
+    """Residency tiers: the whole model stored compressed on disk, a plan
+    under a GPU-memory budget (and a pinned-RAM budget) keeps some units
+    restored or compressed in HBM or compressed in RAM, and one pass over the
+    model restores every unit in order. Reports the pass time per budget, the
+    trade-off of "Keeping some weights close" (Table 1 of "Why Weight
+    Offloading Slows Inference") on this machine."""
+    import torch
+
+    from lossless_bf16_weight_afx_amd import store, synth, tiers
+
+    specs = synth.model_units(args.layers)
+    path = os.path.join(args.store_dir, f"afx_tiers_{args.layers}l_{os.getpid()}.afxs")
+    st = store.write_store(path, specs, threads=threads, progress=log)
+    try:
+        try:
+            fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+            os.close(fd)
+            direct = True
+        except OSError:
+            direct = False
+        ds = store.DiskStreamer(st, threads=threads, direct=direct)
+        read_s = ds.read_only_s()
+        copy_s = ds.copy_only_s()
+        dec_ms = ds.run()["decode_ms"]
+        del ds
+        torch.cuda.empty_cache()
+        stored = sum(u.bytes for u in st.units)
+        rates = tiers.Rates(read_Bps=stored / read_s, copy_Bps=stored / copy_s, restore_s=[d * 1e-3 for d in dec_ms])
+        log(f"[bench] rates: read {rates.read_Bps / 1e9:.2f} GB/s, copy {rates.copy_Bps / 1e9:.1f} GB/s, "
+            f"restore {sum(dec_ms):.1f} ms per pass")
+        GB = 10 ** 9
+        budgets = [(0, 0), (4 * GB, 0), (8 * GB, 0), (16 * GB, 0), (24 * GB, 0), (32 * GB, 0), (0, 24 * GB),
+                   (4 * GB, 24 * GB)]
+        rows, exact = [], True
+        check_idx = {1, len(st.units) - 2}  # the first and the last layer
+        for gpu_b, host_b in budgets:
+            tier = tiers.plan(st, gpu_b, host_b, rates)
+            tp = tiers.TieredPass(st, tier, threads=threads, direct=direct)
+            ok = []
+            tp.run(on_unit=lambda i, out: ok.append(store.check_unit(out, specs[i])) if i in check_idx else None)
+            exact &= len(ok) == len(check_idx) and all(ok)
+            passes = [tp.run() for _ in range(max(1, args.steps))]
+            pass_s = float(np.median(passes))
+            counts = {t: tier.count(t) for t in tiers.TIERS}
+            rows.append({"gpu_budget_GB": gpu_b / GB, "host_budget_GB": host_b / GB, "tiers": counts,
+                         "hbm_held_GB": round(tp.hbm_bytes() / GB, 2), "pass_s": round(pass_s, 4),
+                         "ready_weight_GBps": round(st.restored_bytes / pass_s / GB, 2),
+                         "model_s": round(sum(tiers.unit_cost_s(t, u.bytes, r, rates)
+                                              for t, u, r in zip(tier, st.units, rates.restore_s)), 4)})
+            log(f"[bench] budget gpu {gpu_b / GB:.0f} GB host {host_b / GB:.0f} GB: {counts}, pass {pass_s:.3f} s")
+            del tp
+            torch.cuda.empty_cache()
+        line = {
+            "metric": "seconds per pass over the model by residency budget on 1 MI355X", "value": rows[0]["pass_s"],
+            "unit": "s", "n_gpus": 1, "steps": args.steps, "warmup": 1, "ms_per_step": round(rows[0]["pass_s"] * 1e3, 1),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+            "config": {"workload": f"qwen3-14b-model-{args.layers}-layers-tiers", "units": len(st.units),
+                       "restored_bytes": st.restored_bytes, "stored_bytes": stored, "o_direct": direct},
+            "bit_exact": bool(exact), "rates": {"read_GBps": round(rates.read_Bps / GB, 3),
+                                                "copy_GBps": round(rates.copy_Bps / GB, 2),
+                                                "restore_ms_per_pass": round(sum(dec_ms), 2)},
+            "budgets": rows, "roofline": None, "cpu_baseline": None,
+        }
+        print(json.dumps(line), flush=True)
+        return 0 if exact else 1
     finally:
         if not args.keep_store:
             os.unlink(path)

@@ -286,3 +286,39 @@ def test_disk_store_read_copy_restore(tmp_path):
     say("[gpu] case disk store: host-unpack pass")
     hs.run(on_unit=lambda i, u, out: ok.append(store.check_unit(out, units_specs[i])))
     assert ok == [True] * len(units_specs)
+
+
+def test_tiers_every_mix_bit_exact(tmp_path):
+    """Units held in all four tiers at once (restored in HBM, compressed in
+    HBM, compressed in pinned RAM, on disk); a pass restores each in order,
+    bit-exact, and a plan under budgets uses only what the budgets allow."""
+    from lossless_bf16_weight_afx_amd import store, tiers
+
+    T = synth.TensorSpec
+    units_specs = [[T(f"r{i}.w", (int(200 + 97 * i), 1024), "normal" if i % 3 else "t4", 60 + i),
+                    T(f"r{i}.n", (1024,), "normal", 80 + i, 1.0, 0.05)] for i in range(9)]
+    path = str(tmp_path / "tiers.afxs")
+    say("[gpu] case tiers: write store")
+    st = store.write_store(path, units_specs, threads=8)
+    try:
+        fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+        os.close(fd)
+        direct = True
+    except OSError:
+        direct = False
+    mix = ["D", "G", "Gc", "H", "D", "D", "H", "Gc", "G"]
+    tp = tiers.TieredPass(st, mix, threads=4, direct=direct)
+    for rep in range(2):
+        ok = []
+        say(f"[gpu] case tiers: mixed pass {rep}")
+        tp.run(on_unit=lambda i, out: ok.append(store.check_unit(out, units_specs[i])))
+        assert ok == [True] * len(units_specs)
+    assert tp.run() > 0
+    r = tiers.Rates(read_Bps=2e9, copy_Bps=50e9, restore_s=[1e-4] * len(st.units))
+    total = sum(u.bytes for u in st.units)
+    assert tiers.plan(st, 0, 0, r) == ["D"] * len(st.units)
+    assert set(tiers.plan(st, 0, 10 * total, r)) == {"H"}
+    assert set(tiers.plan(st, 10 * total, 10 * total, r)) == {"G"}
+    p = tiers.plan(st, total // 2, 0, r)
+    used = sum(u.bytes if t == "Gc" else (2 * u.n_values if t == "G" else 0) for u, t in zip(st.units, p))
+    assert used <= total // 2 and "D" in p
