@@ -143,6 +143,43 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
                const uint8_t code_len[256], uint64_t total_bits, void *blob, size_t blob_bytes,
                int threads);
 
+/* ---- The restore fused into its consumer. "Why Weight Offloading Slows
+ * Inference" (section "Lossless compression") restores the released bits
+ * before computation; for a matrix-vector product the restored matrix need
+ * not reach HBM at all. */
+
+/* afx_restore_gemv_async: y += W x, where W is the tensor of the device blob
+ * (info from afx_query on a host copy), taken as row-major [rows, cols]
+ * (rows * cols == n_elems), x is BF16 [m, cols] and y FP32 [m, rows], both
+ * row-major in device memory; m is 1, 2 or 4. W is restored chunk by chunk
+ * in registers and LDS and never written out. Products of two BF16 values
+ * are exact in FP32; the sums are FP32 and added into y with atomic adds,
+ * so their order (and the last bits) may differ between calls. The caller
+ * owns y and its initial contents. Enqueued on stream; returns without
+ * waiting. Errors: as afx_decode_layer_async; AFX_E_INVALID_ARG (rows *
+ * cols != n_elems, NULL pointer), AFX_E_UNSUPPORTED (cols not a multiple of
+ * 8 or above 2^32 - 1; m not 1, 2 or 4), AFX_E_MISALIGNED (blob or x not
+ * 16-byte aligned, y not 4-byte aligned). */
+int afx_restore_gemv_async(const afx_info *info, const void *blob_dev, uint64_t rows, uint64_t cols,
+                           const uint16_t *x_dev, uint32_t m, float *y_dev, void *stream);
+
+#define AFX_MAX_GEMV_JOBS_PER_LAUNCH 16u
+
+/* One matrix of a batch of products (e.g. the seven of a decoder layer). */
+typedef struct afx_gemv_job {
+    const afx_info *info;  /* filled by afx_query from a host copy of the blob */
+    const void *blob_dev;  /* device copy of the same blob, 16-byte aligned */
+    uint64_t rows, cols;   /* W is row-major [rows, cols], rows * cols == n_elems */
+    const uint16_t *x_dev; /* BF16 [m, cols], 16-byte aligned */
+    float *y_dev;          /* FP32 [m, rows], added into, 4-byte aligned */
+} afx_gemv_job;
+
+/* afx_restore_gemv_batch_async: afx_restore_gemv_async for every job (all
+ * with the same m), one launch per AFX_MAX_GEMV_JOBS_PER_LAUNCH jobs; all
+ * jobs are checked before anything is enqueued. Errors as
+ * afx_restore_gemv_async. */
+int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream);
+
 /* ---- Unpack on the host. "Why Weight Offloading Slows Inference" (section
  * "The path from storage to the GPU", Figure 1) unpacks a compressed weight
  * in RAM between the read and the copy to the GPU, and section "Lossless

@@ -28,7 +28,8 @@ AFX_READ_DIRECT = 1
 
 # Every symbol include/afx.h declares.
 EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_status_str",
-           "afx_encode_plan", "afx_encode", "afx_file_read", "afx_decode_host")
+           "afx_encode_plan", "afx_encode", "afx_file_read", "afx_decode_host",
+           "afx_restore_gemv_async", "afx_restore_gemv_batch_async")
 
 
 class AfxError(RuntimeError):
@@ -60,6 +61,17 @@ class afx_info(ctypes.Structure):
         ("off_gap", ctypes.c_uint64),
         ("off_signmant", ctypes.c_uint64),
         ("off_exp", ctypes.c_uint64),
+    ]
+
+
+class afx_gemv_job(ctypes.Structure):
+    _fields_ = [
+        ("info", ctypes.POINTER(afx_info)),
+        ("blob_dev", ctypes.c_void_p),
+        ("rows", ctypes.c_uint64),
+        ("cols", ctypes.c_uint64),
+        ("x_dev", ctypes.c_void_p),
+        ("y_dev", ctypes.c_void_p),
     ]
 
 
@@ -104,6 +116,13 @@ def lib() -> ctypes.CDLL:
         L.afx_file_read.restype = ctypes.c_int
         L.afx_decode_host.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
         L.afx_decode_host.restype = ctypes.c_int
+        L.afx_restore_gemv_async.argtypes = [ctypes.POINTER(afx_info), ctypes.c_void_p, ctypes.c_uint64,
+                                             ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+        L.afx_restore_gemv_async.restype = ctypes.c_int
+        L.afx_restore_gemv_batch_async.argtypes = [ctypes.POINTER(afx_gemv_job), ctypes.c_size_t, ctypes.c_uint32,
+                                                   ctypes.c_void_p]
+        L.afx_restore_gemv_batch_async.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -198,6 +217,32 @@ def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None, plan=None)
                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), bits, ctypes.c_void_p(addr),
                             cap, threads), "afx_encode")
     return out[:nbytes] if isinstance(out, np.ndarray) else nbytes
+
+
+def afx_restore_gemv_async(info: afx_info, blob_dev: int, rows: int, cols: int, x_dev: int, m: int, y_dev: int,
+                           stream: int = 0) -> None:
+    """y += W x with W restored on the fly from its device blob (see afx.h)."""
+    _check(lib().afx_restore_gemv_async(ctypes.byref(info), ctypes.c_void_p(blob_dev), rows, cols,
+                                        ctypes.c_void_p(x_dev), m, ctypes.c_void_p(y_dev), ctypes.c_void_p(stream)),
+           "afx_restore_gemv_async")
+
+
+def make_gemv_jobs(jobs) -> ctypes.Array:
+    """Pack (info, blob_dev, rows, cols, x_dev, y_dev) tuples into an
+    afx_gemv_job array (which refers to the afx_info objects: keep them)."""
+    arr = (afx_gemv_job * len(jobs))()
+    for i, (info, blob_dev, rows, cols, x_dev, y_dev) in enumerate(jobs):
+        arr[i].info = ctypes.pointer(info)
+        arr[i].blob_dev, arr[i].rows, arr[i].cols = blob_dev, rows, cols
+        arr[i].x_dev, arr[i].y_dev = x_dev, y_dev
+    return arr
+
+
+def afx_restore_gemv_batch_async(jobs, m: int, stream: int = 0) -> None:
+    """y += W x for every job of a batch (array from make_gemv_jobs, or tuples)."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else make_gemv_jobs(jobs)
+    _check(lib().afx_restore_gemv_batch_async(arr, len(arr), m, ctypes.c_void_p(stream)),
+           "afx_restore_gemv_batch_async")
 
 
 def afx_decode_host(blob, blob_bytes: int | None = None, out=None, threads: int = 0):

@@ -1,0 +1,371 @@
+// afx_device.h -- device pieces shared by the restore kernel and the fused
+// restore-and-multiply kernel (gfx950): the decode table, the staging of a
+// chunk's code words in LDS, the decoding chains, and the loads that feed
+// them. Not installed; included by the .hip sources of libafx.
+//
+// A tensor's exponent codes come in chunks of 4096 elements, each starting at
+// a recorded bit base, with the start of every 32-element group recorded as a
+// gap from its chunk's base; "Why Weight Offloading Slows Inference" (section
+// "Lossless compression") gives the exponent the shorter codes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "afx_internal.h"
+
+namespace afx {
+namespace {
+
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 16;  // one workgroup fills a CU (4 waves per SIMD)
+constexpr int kWavesPerEU = 4;
+constexpr int kSymbolWaves = 256 / kWave;  // waves that hold one exponent value per lane
+constexpr int kThreads = kWave * kWavesPerBlock;
+constexpr int kLutEntries = 1 << kMaxLen;  // 4096
+
+struct TensorDesc {
+    const uint8_t *code_len;
+    const uint64_t *chunk_base;
+    const uint16_t *gap;
+    const uint8_t *signmant;
+    const uint32_t *exp;
+    uint16_t *out;
+    uint64_t n;
+    uint64_t exp_words;
+    uint64_t last_word4;   // highest 4-aligned word index w with w + 4 <= exp_words
+    uint32_t n_chunks;     // ceil(n / 4096)
+    uint32_t blk_lo;       // workgroups [blk_lo, blk_hi) of the grid serve this tensor
+    uint32_t blk_hi;
+    uint32_t reserved;
+};
+
+struct LutScratch {
+    uint32_t wave_count[kSymbolWaves][kMaxLen + 1];  // symbols of each length per wave
+    uint32_t base[kMaxLen + 1];  // position in `sorted` of code 0 of each length, mod 2^32
+    uint8_t sorted[256];         // used symbols in (length, value) order
+};
+
+// Per-wave LDS: the chunk's code words while decoding, then its decoded
+// exponent bytes (4 KB) while storing. A chunk spans at most 4096 * 12 bits;
+// add the alignment slack of the start and the over-read of the last group.
+// Words are staged in reverse order (stream word j at index kRev - j), plus
+// one pad word above, so that one counter gives both the LDS address and the
+// funnel-shift amount of a 32-bit window (see Chain).
+constexpr uint32_t kStageWords = 1568;
+constexpr uint32_t kRev = kStageWords - 1;  // == 3 (mod 4): 16-byte aligned reversed stores
+static_assert(kRev % 4 == 3, "reversed staging needs kRev = 3 mod 4");
+// Each wave's slice, with the pad word, rounded up to 16 bytes so that every
+// slice starts 16-byte aligned.
+constexpr uint32_t kStageRow = (kStageWords + 1 + 3) & ~3u;
+
+// Order LDS traffic between lanes of one wave (no workgroup barrier needed).
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Build the decode table of one canonical code: entry i (a 12-bit window of
+// the stream, MSB first) holds (symbol << 8) | length of the code word that
+// starts the window. The length sits in the low bits so that a 32-bit shift
+// by the whole entry consumes exactly the code (the hardware reads only the
+// low 5 bits of a shift amount). All 1024 threads take part: thread s < 256
+// owns symbol s and passes its code length (the others pass 0), then every
+// thread s fills table entries [4 s, 4 s + 4). Callers bracket it with
+// barriers.
+__device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
+    const int s = threadIdx.x;
+    const int lane = s & (kWave - 1), wave = s / kWave;
+    uint32_t rank = 0;  // among same-length symbols of this wave with smaller value
+    if (len > kMaxLen) len = 0;  // only a corrupt blob gets here; treat as unused
+    if (wave < kSymbolWaves) {
+#pragma unroll
+        for (uint32_t l = 1; l <= kMaxLen; ++l) {
+            const uint64_t m = __ballot(len == l);
+            if (len == l) rank = (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (lane == 0) S.wave_count[wave][l] = (uint32_t)__popcll(m);
+        }
+    }
+    __syncthreads();
+
+    // Every wave derives the canonical code in registers: lane l (1..12)
+    // holds the number of symbols of length l (cnt) and of them in waves
+    // before this one (below), the position of the first of them in
+    // (length, value) order (start), their first code (first) and the end of
+    // their slice of the 12-bit index space (limit).
+    const uint32_t ll = (uint32_t)lane;
+    uint32_t cnt = 0, below = 0;
+    if (ll >= 1 && ll <= kMaxLen) {
+#pragma unroll
+        for (int w = 0; w < kSymbolWaves; ++w) {
+            const uint32_t c = S.wave_count[w][ll];
+            cnt += c;
+            below += w < wave ? c : 0u;
+        }
+    }
+    uint32_t start = 0, first = 0;
+#pragma unroll
+    for (uint32_t m = 1; m < kMaxLen; ++m) {
+        const uint32_t cm = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)m);
+        if (m < ll) {
+            start += cm;
+            first += cm << (ll - m);  // first[l] = (first[l-1] + cnt[l-1]) << 1, unrolled
+        }
+    }
+    const uint32_t limit = (first + cnt) << (kMaxLen - (ll <= kMaxLen ? ll : kMaxLen));
+    // (all lanes active: a lane reads another lane's register)
+    const uint32_t pos = (uint32_t)__shfl((int)start, (int)len) + (uint32_t)__shfl((int)below, (int)len) + rank;
+    if (len) S.sorted[pos & 255] = (uint8_t)s;
+    if (wave == 0 && ll >= 1 && ll <= kMaxLen) S.base[ll] = start - first;
+    __syncthreads();
+
+    // An entry's length is one more than the number of length slices that
+    // end at or before it; its symbol follows from the code's distance to
+    // that length's first code.
+    uint32_t lim[kMaxLen];
+#pragma unroll
+    for (uint32_t q = 1; q < kMaxLen; ++q) lim[q] = (uint32_t)__builtin_amdgcn_readlane((int)limit, (int)q);
+    auto entry = [&](uint32_t idx) -> uint32_t {
+        uint32_t l = 1;
+#pragma unroll
+        for (uint32_t q = 1; q < kMaxLen; ++q) l += idx >= lim[q] ? 1u : 0u;
+        const uint32_t j = S.base[l] + (idx >> (kMaxLen - l));
+        return ((uint32_t)S.sorted[j & 255] << 8) | l;
+    };
+    constexpr uint32_t kPer = kLutEntries / kThreads;  // 4 entries per thread
+    const uint32_t i0 = (uint32_t)s * kPer;
+    const uint32_t e0 = entry(i0);
+    if ((e0 & 0xFF) <= kMaxLen - 2) {
+        // a code of <= 10 bits owns whole 4-aligned blocks of the index space
+        const uint32_t d = e0 | (e0 << 16);
+        *reinterpret_cast<uint2 *>(lut + i0) = make_uint2(d, d);
+    } else {
+        for (uint32_t j = 0; j < kPer; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
+    }
+}
+
+// Two BF16 values from the sign/mantissa bytes b and exponent bytes e of
+// elements 0,1 (kHigh: of elements 2,3). With v = [e1 b1 e0 b0], each 16-bit
+// half of v is (e << 8) | (s << 7) | m; the result half is
+// (s << 15) | (e << 7) | m.
+template <bool kHigh>
+__device__ inline uint32_t join_pair(uint32_t b, uint32_t e) {
+    // b2, e2: the two elements' bytes in 16-bit lanes. The result half is
+    // (e << 7) + m + (s << 15) = (e << 7) + b + 255 * (b & 0x80), and no
+    // half overflows into the next.
+    constexpr uint32_t sel = kHigh ? 0x0c030c02u : 0x0c010c00u;
+    const uint32_t b2 = __builtin_amdgcn_perm(0u, b, sel);
+    const uint32_t e2 = __builtin_amdgcn_perm(0u, e, sel);
+    return (e2 << 7) + (__umul24(b2 & 0x00800080u, 255u) + b2);
+}
+
+// Symbols (byte 1 of two table entries) packed as bytes 0,1 of a word.
+__device__ inline uint32_t sym_pair(uint32_t e1, uint32_t e2) { return __builtin_amdgcn_perm(e2, e1, 0x0c0c0501u); }
+// Bytes 0,1 of lo and of hi as the four bytes of a word.
+__device__ inline uint32_t join_halves(uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x05040100u); }
+
+// One decoding chain. With P the bit position in the staged words (MSB
+// first), the chain keeps r = 32 * kRev - P. Then the next 32 stream bits are
+// the funnel shift of staged words [r/32 + 1] (high) and [r/32] (low) by
+// r mod 32, and consuming a code of length l is r -= l.
+struct Chain {
+    uint32_t r;
+};
+
+__device__ inline uint32_t window(const uint32_t *stage, uint32_t r) {
+    const uint32_t *p = stage + (r >> 5);
+    return __builtin_amdgcn_alignbit(p[1], p[0], r);
+}
+
+__device__ inline uint32_t lookup(const uint16_t *lut, uint32_t win) { return lut[win >> (32 - kMaxLen)]; }
+
+// Decode two symbols from one 32-bit window (two codes take at most 24 bits)
+// and return them as bytes 0,1.
+__device__ inline uint32_t chain_pair(Chain &c, const uint32_t *stage, const uint16_t *lut) {
+    const uint32_t win = window(stage, c.r);
+    const uint32_t e1 = lookup(lut, win);
+    const uint32_t e2 = lookup(lut, win << (e1 & 31));
+    c.r -= (e1 + e2) & 0xFF;
+    return sym_pair(e1, e2);
+}
+
+// The same chain with the two staged words of its window and the word after
+// them kept in registers: the next word is read one pair ahead, so a pair
+// costs two dependent table reads instead of three LDS round trips. Chains A
+// and B advance together so that their reads overlap.
+struct BufChain {
+    uint32_t r, hi, lo, nx;
+};
+
+__device__ inline BufChain buf_chain(const uint32_t *stage, uint32_t r) {
+    const uint32_t *p = stage + (r >> 5);
+    return BufChain{r, p[1], p[0], p[-1]};
+}
+
+__device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t *stage, const uint16_t *lut,
+                                       uint32_t &sa, uint32_t &sb) {
+    const uint32_t wa = __builtin_amdgcn_alignbit(a.hi, a.lo, a.r);
+    const uint32_t wb = __builtin_amdgcn_alignbit(b.hi, b.lo, b.r);
+    const uint32_t a1 = lookup(lut, wa), b1 = lookup(lut, wb);
+    const uint32_t a2 = lookup(lut, wa << (a1 & 31)), b2 = lookup(lut, wb << (b1 & 31));
+    const uint32_t da = (a1 + a2) & 0xFF, db = (b1 + b2) & 0xFF;
+    const bool ca = (a.r & 31) < da, cb = (b.r & 31) < db;  // the window moved to the next word
+    a.r -= da;
+    b.r -= db;
+    a.hi = ca ? a.lo : a.hi;
+    b.hi = cb ? b.lo : b.hi;
+    a.lo = ca ? a.nx : a.lo;
+    b.lo = cb ? b.nx : b.lo;
+    a.nx = stage[(a.r >> 5) - 1];
+    b.nx = stage[(b.r >> 5) - 1];
+    sa = sym_pair(a1, a2);
+    sb = sym_pair(b1, b2);
+}
+
+__device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Where a chunk's code bits lie among the stream words.
+struct ChunkGeom {
+    uint64_t w0;      // first staged stream word (16-byte aligned)
+    uint32_t nwords;  // words to stage: through the chunk's last bit plus over-read slack
+    uint32_t rel;     // the chunk's first bit, counted from word w0
+};
+
+__device__ inline ChunkGeom chunk_geom(uint64_t base, uint64_t end) {
+    ChunkGeom g;
+    g.w0 = (base >> 5) & ~(uint64_t)3;
+    // unsigned arithmetic saturates through the min on a corrupt base pair
+    const uint64_t want = ((end + 31) >> 5) + 16 - g.w0;
+    g.nwords = (uint32_t)umin64(want, kStageWords);
+    g.rel = (uint32_t)(base - (g.w0 << 5));  // < 128
+    return g;
+}
+
+// The first 512 staged words of a chunk travel through registers so that
+// their loads can be issued one chunk ahead; longer chunks (more than about
+// 4 bits per element) fetch the rest when they are staged.
+constexpr uint32_t kPrefetchWords = 2 * 4 * kWave;
+
+struct StreamRegs {
+    uint4 v[2];
+};
+
+// Four stream words from 4-aligned index g. Past the end of the section the
+// index is clamped: such words lie beyond the last code bit (the stream ends
+// with four zero words), so what they hold never reaches an output.
+__device__ inline uint4 load_words4(const TensorDesc &T, uint64_t g) {
+    return *reinterpret_cast<const uint4 *>(T.exp + umin64(g, T.last_word4));
+}
+
+// Only the words the chunk needs are requested (typical chunks need ~350).
+__device__ inline void load_stream(const TensorDesc &T, const ChunkGeom &g, int lane, StreamRegs &s) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t i = 4 * (uint32_t)lane + (uint32_t)k * 4 * kWave;
+        if (i < g.nwords) s.v[k] = load_words4(T, g.w0 + i);
+    }
+}
+
+// Stream word i goes to index kRev - i (reversed; see Chain).
+__device__ inline void put_words4(uint32_t *stage, uint32_t i, uint4 v) {
+    *reinterpret_cast<uint4 *>(stage + (kRev - 3 - i)) = make_uint4(v.w, v.z, v.y, v.x);
+}
+
+__device__ inline void put_stream(const TensorDesc &T, const ChunkGeom &g, const StreamRegs &s, uint32_t *stage,
+                                  int lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t i = 4 * (uint32_t)lane + (uint32_t)k * 4 * kWave;
+        if (i < g.nwords) put_words4(stage, i, s.v[k]);
+    }
+    for (uint32_t i = kPrefetchWords + 4 * (uint32_t)lane; i < g.nwords; i += 4 * kWave)
+        put_words4(stage, i, load_words4(T, g.w0 + i));
+}
+
+__device__ inline uint32_t readlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+
+// Chunk bases are fetched with a vector load (lane 0: start, lane 1: end of
+// chunk lc) so that waiting for them never involves the LDS counter.
+__device__ inline uint64_t load_bases(const TensorDesc &T, uint64_t lc, int lane) {
+    return T.chunk_base[lc + (uint64_t)(lane & 1)];
+}
+__device__ inline ChunkGeom geom_from_lanes(uint64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint64_t base = ((uint64_t)readlane(hi, 0) << 32) | readlane(lo, 0);
+    const uint64_t end = ((uint64_t)readlane(hi, 1) << 32) | readlane(lo, 1);
+    return chunk_geom(base, end);
+}
+
+struct Gaps {
+    uint32_t a, b;  // start of groups lane and lane + 64, relative to the chunk
+};
+
+// Groups past the end of a short last chunk take the last group's gap: they
+// decode something, but nothing they decode is stored.
+__device__ inline Gaps load_gaps(const TensorDesc &T, uint64_t lc, int lane) {
+    const uint32_t ng = (uint32_t)((umin64(kChunk, T.n - lc * kChunk) + kGroup - 1) / kGroup);
+    const uint16_t *gap = T.gap + lc * kGroupsPerChunk;
+    // read once: not kept in the caches
+    return Gaps{__builtin_nontemporal_load(gap + min((uint32_t)lane, ng - 1)),
+                __builtin_nontemporal_load(gap + min((uint32_t)lane + kWave, ng - 1))};
+}
+
+// 16 output bytes; the output is written once and not read back here, so the
+// stores bypass cache allocation (each store instruction covers whole lines).
+__device__ inline void store_out(uint16_t *p, uint4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
+}
+
+// Decode a staged chunk's 4096 exponent codes and leave the exponent bytes
+// in element order at the start of `stage` (which held the code words).
+// Chain starts are clamped so that 32 decodes (at most 384 bits) never leave
+// the staged words even on a corrupt gap; the buffered chains' read ahead
+// (one word past the window) stays at index >= 0 for the same reason.
+// kBuffered picks the buffered chains (the choice of a kernel whose chunk
+// time the decode latency bounds; the restore, bound by HBM, does not need
+// them).
+template <bool kBuffered = false>
+__device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, const uint16_t *lut, uint32_t *stage,
+                                        int lane) {
+    constexpr uint32_t kMaxStart = 32 * (kRev - 13);
+    const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart);
+    const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart);
+    uint32_t wa[8], wb[8];
+    if (kBuffered) {
+        BufChain A = buf_chain(stage, ra), B = buf_chain(stage, rb);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            uint32_t a01, b01, a23, b23;
+            buf_chain_pairs(A, B, stage, lut, a01, b01);
+            buf_chain_pairs(A, B, stage, lut, a23, b23);
+            wa[q] = join_halves(a01, a23);
+            wb[q] = join_halves(b01, b23);
+        }
+    } else {
+        Chain A{ra};
+        Chain B{rb};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t a01 = chain_pair(A, stage, lut);
+            const uint32_t b01 = chain_pair(B, stage, lut);
+            const uint32_t a23 = chain_pair(A, stage, lut);
+            const uint32_t b23 = chain_pair(B, stage, lut);
+            wa[q] = join_halves(a01, a23);
+            wb[q] = join_halves(b01, b23);
+        }
+    }
+    wave_sync();  // every lane is done reading the staged words
+    uint4 *pa = reinterpret_cast<uint4 *>(stage + lane * 8);
+    uint4 *pb = reinterpret_cast<uint4 *>(stage + (lane + kWave) * 8);
+    pa[0] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    pa[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
+    pb[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    pb[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
+    wave_sync();
+}
+
+}  // namespace
+}  // namespace afx

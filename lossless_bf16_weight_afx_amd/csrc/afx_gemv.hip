@@ -1,0 +1,367 @@
+// afx_gemv.hip -- the restore fused into its consumer (gfx950): y += W x for a
+// weight matrix W held only in its coded form.
+//
+// "Why Weight Offloading Slows Inference" (section "Lossless compression")
+// restores the released bits of a compressed weight before computation.
+// Restoring into HBM and then multiplying writes the BF16 matrix (2 bytes per
+// value) and reads it back; for the matrix-vector products of token-by-token
+// generation, which read every weight once per token, that traffic is the
+// cost. Here each wave restores a chunk exactly as afx_decode.hip does, up to
+// the exponent bytes in LDS, and multiplies the restored values by the
+// activations in registers: HBM sees the coded matrix (~1.39 bytes per value)
+// and nothing else.
+//
+// W is row-major [rows, cols] (the blob's element order), x is BF16 [m, cols]
+// and y is FP32 [m, rows], both row-major; m is 1, 2 or 4 (a handful of
+// tokens). The products of two BF16 values are exact in FP32; sums are FP32,
+// per lane over 8 consecutive values, then across the wave, then into y with
+// atomic adds (in no fixed order).
+//
+// Work decomposition as in the restore: one 16-wave workgroup per CU, chunks
+// round the workgroups, claimed one at a time by the waves from an LDS
+// counter, code words staged a chunk ahead.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "afx_device.h"
+
+namespace afx {
+namespace {
+
+struct GemvArgs {
+    TensorDesc t;       // t.blk_lo/blk_hi: the workgroups that serve this matrix
+    const uint16_t *x;  // [m, cols] BF16
+    float *y;           // [m, rows] FP32, accumulated into
+    uint64_t rows;
+    uint32_t cols;      // a multiple of 8: every 8 consecutive values lie in one row
+    uint32_t reserved;
+};
+
+constexpr uint32_t kMaxGemvJobs = AFX_MAX_GEMV_JOBS_PER_LAUNCH;
+
+struct GemvBatch {
+    GemvArgs j[kMaxGemvJobs];
+    uint32_t n;
+};
+
+__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Sum over the wave with DPP moves (no LDS); the total lands in lane 63.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ inline float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+__device__ inline float wave_sum_to_lane63(float v) {
+    v = dpp_add<0xB1>(v);         // quad_perm [1,0,3,2]: pairs
+    v = dpp_add<0x4E>(v);         // quad_perm [2,3,0,1]: quads
+    v = dpp_add<0x141>(v);        // row_half_mirror: 8 lanes
+    v = dpp_add<0x140>(v);        // row_mirror: rows of 16
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Activations of one matrix staged in LDS when they fit (m * cols BF16).
+constexpr uint32_t kXStageBytes = 48 * 1024;
+
+// Request chunk lc's sign/mantissa bytes in store order (lane: bytes
+// [r*512 + 8*lane, +8) for r = 0..7); read once, not kept in the caches.
+__device__ inline void load_signmant(const TensorDesc &T, uint64_t lc, int lane, uint2 (&smv)[8]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint64_t e0 = lc * kChunk;
+    const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
+    const uint8_t *sm = T.signmant + e0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sm + (i + 8 <= ne ? i : 0)));
+        smv[r] = make_uint2(t.x, t.y);  // tail elements are reread below
+    }
+}
+
+// Restore chunk lc of W and add its products with x into y. smv holds (or
+// is receiving) chunk lc's sign/mantissa bytes on entry; as soon as they
+// have been used, the bytes of chunk next_lc (if any) are requested into it,
+// so that their latency overlaps the rest of this chunk and the next decode.
+template <int M>
+__device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t lc, uint2 (&smv)[8],
+                                  bool has_next, uint64_t next_lc, const ChunkGeom &g, const Gaps &gaps,
+                                  const uint16_t *lut, uint32_t *stage, int lane, uint64_t later_bases,
+                                  ChunkGeom &later) {
+    const TensorDesc &T = a.t;
+    const uint64_t e0 = lc * kChunk;
+    const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
+    const uint8_t *sm = T.signmant + e0;
+    decode_exponents<true>(g, gaps, lut, stage, lane);
+    asm volatile("" : "+v"(later_bases));  // not before the decode above
+    later = geom_from_lanes(later_bases);
+
+    // The chunk starts in row row0 at column c0; lane handles values
+    // [r*512 + 8*lane, +8) for r = 0..7, which lie in one row.
+    const uint64_t row0 = e0 / a.cols;
+    const uint32_t c0 = (uint32_t)(e0 - row0 * a.cols);
+    const uint8_t *exb = reinterpret_cast<const uint8_t *>(stage);
+    float acc[8][M];
+    uint32_t drow[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
+        uint32_t col = c0 + i;
+        const uint32_t d = a.cols >= kChunk ? (col >= a.cols ? 1u : 0u) : col / a.cols;
+        col -= d * a.cols;
+        drow[r] = d;
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+        if (i + 8 <= ne) {
+            const uint2 b = smv[r];
+            const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
+            const uint32_t w01 = join_pair<false>(b.x, e.x), w23 = join_pair<true>(b.x, e.x);
+            const uint32_t w45 = join_pair<false>(b.y, e.y), w67 = join_pair<true>(b.y, e.y);
+            const float w[8] = {bf16_lo(w01), bf16_hi(w01), bf16_lo(w23), bf16_hi(w23),
+                                bf16_lo(w45), bf16_hi(w45), bf16_lo(w67), bf16_hi(w67)};
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 xv = *reinterpret_cast<const uint4 *>(x + (uint64_t)m * a.cols + col);
+                float s = w[0] * bf16_lo(xv.x);
+                s = fmaf(w[1], bf16_hi(xv.x), s);
+                s = fmaf(w[2], bf16_lo(xv.y), s);
+                s = fmaf(w[3], bf16_hi(xv.y), s);
+                s = fmaf(w[4], bf16_lo(xv.z), s);
+                s = fmaf(w[5], bf16_hi(xv.z), s);
+                s = fmaf(w[6], bf16_lo(xv.w), s);
+                s = fmaf(w[7], bf16_hi(xv.w), s);
+                acc[r][m] = s;
+            }
+        } else {
+            for (uint32_t j = i; j < ne && j < i + 8; ++j) {
+                const uint32_t bb = sm[j], ee = exb[j];
+                const float w = __uint_as_float((((bb & 0x80u) << 8) | (ee << 7) | (bb & 0x7Fu)) << 16);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    acc[r][m] = fmaf(w, __uint_as_float((uint32_t)x[(uint64_t)m * a.cols + col + (j - i)] << 16),
+                                     acc[r][m]);
+            }
+        }
+    }
+    if (has_next) load_signmant(T, next_lc, lane, smv);
+    // Sum each row's products over the wave and add them into y.
+    const uint32_t nrows = (c0 + ne - 1) / a.cols + 1;
+    for (uint32_t d = 0; d < nrows; ++d) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float s = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) s += drow[r] == d ? acc[r][m] : 0.f;
+            s = wave_sum_to_lane63(s);
+            if (lane == kWave - 1) atomicAdd(a.y + (uint64_t)m * a.rows + row0 + d, s);
+        }
+    }
+}
+
+template <int M>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void afx_gemv_kernel(const GemvBatch batch) {
+    __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];                   // 8 KB
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][kStageRow];  // 98 KB
+    __shared__ LutScratch scratch;
+    __shared__ uint32_t next_j;  // the workgroup's next unclaimed chunk of the matrix
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kXStageBytes / 2];
+
+    int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t b = blockIdx.x;
+    uint32_t *my_stage = stage[wave];
+    for (uint32_t t = 0; t < batch.n; ++t) {
+        const GemvArgs &a = batch.j[t];
+        const TensorDesc &T = a.t;
+        // Workgroups [blk_lo, blk_hi) serve this matrix; the k-th of nb takes
+        // chunks k + j nb; wave w starts with j = w and j = w + 16, then
+        // claims the next unclaimed j.
+        if (b < T.blk_lo || b >= T.blk_hi) continue;
+        const uint32_t k = b - T.blk_lo, nb = T.blk_hi - T.blk_lo;
+        if (k >= T.n_chunks) continue;
+        const uint32_t mine = (T.n_chunks - k + nb - 1) / nb;
+        uint32_t jc = wave, jn = wave + kWavesPerBlock;
+        const bool has_c = jc < mine;
+        bool has_n = jn < mine;
+        const uint32_t len = wave < kSymbolWaves ? T.code_len[threadIdx.x] : 0;
+        uint64_t bases_c = 0, bases_n = 0;
+        Gaps gaps{0, 0};
+        if (has_c) bases_c = load_bases(T, k + (uint64_t)jc * nb, lane);
+        if (has_n) bases_n = load_bases(T, k + (uint64_t)jn * nb, lane);
+        if (has_c) gaps = load_gaps(T, k + (uint64_t)jc * nb, lane);
+        ChunkGeom g{};
+        StreamRegs s;
+        if (has_c) {
+            g = geom_from_lanes(bases_c);
+            load_stream(T, g, lane, s);
+        }
+        __syncthreads();  // every wave is done with the previous table, counter and activations
+        if (threadIdx.x == 0) next_j = 2 * kWavesPerBlock;
+        // stage the activations (read by every chunk) when they fit
+        const uint64_t xbytes = (uint64_t)M * a.cols * 2;
+        const bool x_in_lds = xbytes <= kXStageBytes;
+        if (x_in_lds)
+            for (uint32_t i = threadIdx.x; i < xbytes / 16; i += kThreads)
+                reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(a.x)[i];
+        build_lut(len, lut, scratch);  // ends with a barrier
+        __syncthreads();
+        if (!has_c) continue;
+        const uint16_t *x = x_in_lds ? xs : a.x;
+        uint2 smv[8];
+        load_signmant(T, k + (uint64_t)jc * nb, lane, smv);
+        put_stream(T, g, s, my_stage, lane);
+        wave_sync();
+        ChunkGeom gn = geom_from_lanes(bases_n);
+        while (true) {
+            asm volatile("" : "+v"(lane));
+            uint32_t jnn = ~0u;
+            bool has_nn = false;
+            StreamRegs sn;
+            Gaps gaps_n{0, 0};
+            uint64_t bases_nn = 0;
+            if (has_n) {
+                uint32_t v = 0;
+                if (lane == 0) v = atomicAdd(&next_j, 1u);
+                jnn = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+                has_nn = jnn < mine;
+                load_stream(T, gn, lane, sn);
+                gaps_n = load_gaps(T, k + (uint64_t)jn * nb, lane);
+                if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
+            }
+            ChunkGeom gnn;
+            gemv_chunk<M>(a, x, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, lut, my_stage,
+                          lane, bases_nn, gnn);
+            if (!has_n) break;
+            wave_sync();  // the exponent bytes have been read
+            put_stream(T, gn, sn, my_stage, lane);
+            wave_sync();
+            g = gn;
+            gaps = gaps_n;
+            gn = gnn;
+            jc = jn;
+            jn = jnn;
+            has_n = has_nn;
+        }
+    }
+}
+
+std::atomic<int> g_gemv_blocks[64];
+
+template <int M>
+int gemv_max_blocks(int *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return AFX_E_HIP;
+    if (dev < 0 || dev >= 64) return AFX_E_UNSUPPORTED;
+    int v = g_gemv_blocks[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return AFX_E_HIP;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, afx_gemv_kernel<M>, kThreads, 0) != hipSuccess)
+            return AFX_E_HIP;
+        v = std::max(1, cus) * std::max(1, per_cu);
+        g_gemv_blocks[dev].store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return AFX_OK;
+}
+
+// One launch for up to kMaxGemvJobs checked matrices: the grid is split
+// among them in proportion to their chunk counts, as for a restore batch.
+template <int M>
+int launch_gemv(GemvBatch &batch, hipStream_t stream) {
+    uint64_t total = 0, first[kMaxGemvJobs];
+    for (uint32_t t = 0; t < batch.n; ++t) {
+        first[t] = total;
+        total += batch.j[t].t.n_chunks;
+    }
+    if (total == 0) return AFX_OK;
+    int max_blocks = 0;
+    const int rc = gemv_max_blocks<M>(&max_blocks);
+    if (rc != AFX_OK) return rc;
+    const uint64_t per_block = (total + max_blocks - 1) / max_blocks;
+    const uint64_t grid = std::max<uint64_t>(1, (total + per_block - 1) / per_block);
+    for (uint32_t t = 0; t < batch.n; ++t) {
+        const uint64_t lo = grid * first[t] / total;
+        uint64_t hi = grid * (first[t] + batch.j[t].t.n_chunks) / total;
+        if (hi <= lo) hi = lo + 1;
+        batch.j[t].t.blk_lo = (uint32_t)lo;
+        batch.j[t].t.blk_hi = (uint32_t)hi;
+    }
+    hipLaunchKernelGGL(afx_gemv_kernel<M>, dim3((unsigned)grid), dim3(kThreads), 0, stream, batch);
+    return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
+}
+
+int check_gemv_job(const afx_gemv_job &j, uint32_t m) {
+    int rc = check_info(j.info);
+    if (rc != AFX_OK) return rc;
+    const afx_info *info = j.info;
+    if (j.cols == 0 || info->n_elems % j.cols || info->n_elems / j.cols != j.rows) return AFX_E_INVALID_ARG;
+    if (info->n_elems == 0) return AFX_OK;  // nothing to add
+    if (!j.blob_dev) return AFX_E_INVALID_ARG;
+    if (j.cols % 8 || j.cols > 0xFFFFFFFFull) return AFX_E_UNSUPPORTED;
+    if (m != 1 && m != 2 && m != 4) return AFX_E_UNSUPPORTED;
+    if (!j.x_dev || !j.y_dev) return AFX_E_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(j.blob_dev) | reinterpret_cast<uintptr_t>(j.x_dev)) & 15) return AFX_E_MISALIGNED;
+    if (reinterpret_cast<uintptr_t>(j.y_dev) & 3) return AFX_E_MISALIGNED;
+    return AFX_OK;
+}
+
+GemvArgs gemv_args(const afx_gemv_job &j) {
+    const afx_info *info = j.info;
+    const uint8_t *b = static_cast<const uint8_t *>(j.blob_dev);
+    GemvArgs a;
+    a.t.code_len = b + info->off_code_len;
+    a.t.chunk_base = reinterpret_cast<const uint64_t *>(b + info->off_chunk_base);
+    a.t.gap = reinterpret_cast<const uint16_t *>(b + info->off_gap);
+    a.t.signmant = b + info->off_signmant;
+    a.t.exp = reinterpret_cast<const uint32_t *>(b + info->off_exp);
+    a.t.out = nullptr;
+    a.t.n = info->n_elems;
+    a.t.exp_words = info->exp_words;
+    a.t.last_word4 = (info->exp_words - 4) & ~(uint64_t)3;
+    a.t.n_chunks = (uint32_t)info->n_chunks;
+    a.t.blk_lo = a.t.blk_hi = a.t.reserved = 0;
+    a.x = j.x_dev;
+    a.y = j.y_dev;
+    a.rows = j.rows;
+    a.cols = (uint32_t)j.cols;
+    a.reserved = 0;
+    return a;
+}
+
+}  // namespace
+}  // namespace afx
+
+using namespace afx;
+
+extern "C" int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream) {
+    if (!jobs && n_jobs) return AFX_E_INVALID_ARG;
+    for (size_t i = 0; i < n_jobs; ++i) {
+        const int rc = check_gemv_job(jobs[i], m);
+        if (rc != AFX_OK) return rc;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (size_t i = 0; i < n_jobs;) {
+        GemvBatch batch;
+        batch.n = 0;
+        for (; i < n_jobs && batch.n < kMaxGemvJobs; ++i)
+            if (jobs[i].info->n_elems) batch.j[batch.n++] = gemv_args(jobs[i]);
+        int rc = AFX_OK;
+        switch (m) {
+            case 1: rc = launch_gemv<1>(batch, s); break;
+            case 2: rc = launch_gemv<2>(batch, s); break;
+            default: rc = launch_gemv<4>(batch, s); break;
+        }
+        if (rc != AFX_OK) return rc;
+    }
+    return AFX_OK;
+}
+
+extern "C" int afx_restore_gemv_async(const afx_info *info, const void *blob_dev, uint64_t rows, uint64_t cols,
+                                      const uint16_t *x_dev, uint32_t m, float *y_dev, void *stream) {
+    const afx_gemv_job job{info, blob_dev, rows, cols, x_dev, y_dev};
+    return afx_restore_gemv_batch_async(&job, 1, m, stream);
+}

@@ -197,3 +197,22 @@ def sections(blob: np.ndarray) -> dict:
         "offsets": off,
         "header": h,
     }
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns as float64 values (a BF16 value is the float32 whose
+    upper 16 bits are its pattern)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def restore_gemv(blob: np.ndarray, rows: int, cols: int, x_bits: np.ndarray, threads: int = 1):
+    """y = W x in float64 for the matrix W that the blob restores (row-major
+    [rows, cols]) and BF16 activations x [m, cols]; also the bound that FP32
+    summation in any order stays within: (cols - 1) * 2^-24 * sum |w x| per
+    output. The restore is this module's decoder; the product is numpy's.
+    Returns (y [m, rows], bound [m, rows])."""
+    w = bf16_to_f64(decode(blob, threads=threads)).reshape(rows, cols)
+    x = bf16_to_f64(x_bits).reshape(-1, cols)
+    y = x @ w.T
+    bound = (cols - 1) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+    return y, bound

@@ -1,0 +1,104 @@
+"""GPU parity of the restore fused into a matrix-vector product: y += W x with
+W restored on the fly, against the oracle's float64 product of the restored
+matrix, within the bound that FP32 summation in any order keeps:
+(cols - 1) * 2^-24 * sum |w x| per output."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_bf16_weight_afx_amd import afx, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    afx.lib()
+
+
+def run(w_bits, rows, cols, m, seed, y0=None, dist="normal"):
+    blob = oracle.encode(w_bits, (rows, cols))
+    info = afx.afx_query(blob)
+    dev_blob = afx.to_device(blob)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal((m, cols)).astype(np.float32))
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    y = torch.zeros((m, rows), dtype=torch.float32, device="cuda") if y0 is None else y0.clone()
+    afx.afx_restore_gemv_async(info, dev_blob.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4)
+    if y0 is not None:
+        ref = ref + y0.cpu().numpy().astype(np.float64)
+        bound = bound + np.abs(y0.cpu().numpy().astype(np.float64)) * 2.0 ** -24
+    got = y.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    assert np.all(err <= bound), f"error above the bound: worst ratio {worst}"
+    return worst
+
+
+@pytest.mark.parametrize("rows,cols,m", [
+    (64, 4096, 1),      # one chunk per row
+    (640, 5120, 1),     # rows cross chunk boundaries (q_proj-shaped rows)
+    (640, 5120, 2),
+    (640, 5120, 4),
+    (96, 17408, 4),     # down_proj-shaped rows
+    (333, 1000, 2),     # several rows per chunk, short last chunk
+    (129, 32, 1),       # 128 rows in a chunk
+    (7, 8, 4),          # one tiny chunk
+])
+def test_shapes(rows, cols, m):
+    say(f"[gpu] case gemv {rows}x{cols} m={m}")
+    w = synth.generate(synth.TensorSpec("w", (rows, cols), "normal", rows + cols))
+    worst = run(w, rows, cols, m, seed=rows * 7 + m)
+    say(f"[gpu]   worst error / bound = {worst:.3g}")
+
+
+def test_heavy_tails_and_accumulation():
+    say("[gpu] case gemv t4 weights, y accumulated onto existing values")
+    rows, cols = 300, 5120
+    w = synth.generate(synth.TensorSpec("w", (rows, cols), "t4", 77))
+    y0 = torch.randn((2, rows), dtype=torch.float32, device="cuda")
+    run(w, rows, cols, 2, seed=5, y0=y0)
+
+
+def test_q_proj_full_size():
+    say("[gpu] case gemv 5120x5120 m=1")
+    spec = synth.single_tensor(5120, 5120, 2)[0]
+    run(synth.generate(spec), 5120, 5120, 1, seed=9)
+
+
+def test_batch_of_mixed_matrices_one_launch():
+    """Seven matrices of mixed shapes (a decoder layer's, scaled down) in one
+    batch call, m = 4; every product within its bound."""
+    shapes = [(640, 640), (128, 640), (128, 640), (640, 640), (2176, 640), (2176, 640), (640, 2176)]
+    m = 4
+    rng = np.random.default_rng(31)
+    jobs, keep, refs = [], [], []
+    for t, (rows, cols) in enumerate(shapes):
+        w = synth.generate(synth.TensorSpec(f"w{t}", (rows, cols), "t4" if t == 6 else "normal", 700 + t))
+        blob = oracle.encode(w, (rows, cols))
+        info = afx.afx_query(blob)
+        db = afx.to_device(blob)
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, cols)).astype(np.float32))
+        xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+        y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+        keep.append((info, db, xd, y))
+        jobs.append((info, db.data_ptr(), rows, cols, xd.data_ptr(), y.data_ptr()))
+        refs.append(oracle.restore_gemv(blob, rows, cols, x, threads=4))
+    say("[gpu] case gemv batch of 7 matrices, m=4")
+    afx.afx_restore_gemv_batch_async(jobs, m, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for (info, db, xd, y), (ref, bound), shape in zip(keep, refs, shapes):
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound), shape
