@@ -9,8 +9,10 @@ Default workload: one Qwen3-14B-shaped decoder layer (11 tensors, 330.3M
 BF16 values, 0.66 GB restored), the unit the time-to-ready model of "Why
 Weight Offloading Slows Inference" reasons about. Other workloads:
 tensor-1024 (1024x1024), q_proj (5120x5120), embedding (151936x5120), model
-(the whole 40-layer model, compressed in pinned host memory) and disk (the
-whole model stored compressed in a file, read cold, copied and restored).
+(the whole 40-layer model, compressed in pinned host memory), disk (the
+whole model stored compressed in a file, read cold, copied and restored),
+tiers (the model spread over residency tiers under memory budgets) and gemv
+(the restore fused into the products y += W x of one layer's matrices).
 
 Prints one JSON line with the throughput of restored BF16, the HBM roofline
 fraction of the decode kernel (hipEvent timing on the launch stream), and the
@@ -39,8 +41,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decoded BF16 GB/s on 1 MI355X + % of HBM roofline; bit-exact vs CPU oracle"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_weight_afx_amd", "csrc", "afx_decode.hip")
+CSRC = os.path.join(ROOT, "lossless_bf16_weight_afx_amd", "csrc")
 KERNEL_NAME = "afx_decode_kernel"
+# the sources each kernel is built from (a profile taken on other sources is stale)
+KERNEL_SRCS = {"afx_decode_kernel": ("afx_decode.hip", "afx_device.h"),
+               "afx_gemv_kernel": ("afx_gemv.hip", "afx_device.h")}
+GEMV_METRIC = ("BF16 weight GB/s consumed by the fused restore+GEMV on 1 MI355X + % of HBM roofline; "
+               "within the FP32 summation bound of the CPU oracle")
 
 
 def log(*a):
@@ -68,15 +75,18 @@ def workload_specs(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(kernel: str = KERNEL_NAME) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def profile_traffic(workload: str):
+def profile_traffic(workload: str, kernel: str = KERNEL_NAME):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_pmc.txt")
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -84,7 +94,7 @@ def profile_traffic(workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = (t.strip() for t in line.split("=", 1))
             kv[k] = v
-    if kv.get("kernel_sha") != kernel_sha():
+    if kv.get("kernel_sha") != kernel_sha(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -98,7 +108,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk", "tiers"])
+                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk", "tiers", "gemv"])
+    ap.add_argument("--m", type=int, default=1, choices=[1, 2, 4],
+                    help="activation rows of the fused restore+GEMV (--workload gemv)")
     ap.add_argument("--layers", type=int, default=40,
                     help="decoder layers of the whole model (--workload model or disk)")
     ap.add_argument("--store-dir", default=os.environ.get("TMPDIR") or "/tmp",
@@ -111,8 +123,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the restore is per-tensor work with no collective; "
-              "run it with --gpus 1 (see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the restore is per-tensor work with no collective (on "
+              "several GPUs each restores the tensors of its own shard); run it with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
@@ -131,6 +143,8 @@ def main() -> int:
         return bench_disk(args, threads)
     if args.workload == "tiers":
         return bench_tiers(args, threads)
+    if args.workload == "gemv":
+        return bench_gemv(args, threads)
     workload, specs = workload_specs(args.workload)
 
     # ---- inputs: generate, encode with the library's encoder, move to HBM
@@ -194,30 +208,14 @@ def main() -> int:
     launch_ms = ms_per_step  # one kernel launch per step
     value = restored / (ms_per_step * 1e-3) / 1e9
 
-    # ---- a plain elementwise copy kernel (read N, write N bytes) over the
-    # same traffic and the same rotation: the box's practical ceiling, and the
-    # known-size kernel that calibrates the HBM byte counters of rocprofv3
-    half = traffic_pass // 4  # int16 elements: 2 bytes read + 2 written each
-    src = torch.empty(half * copies, dtype=torch.int16, device=dev)
-    dst = torch.empty_like(src)
-    torch.bitwise_not(src, out=dst)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_copy = max(10, copies)
-    c0.record(stream)
-    for k in range(n_copy):
-        sl = slice((k % copies) * half, (k % copies + 1) * half)
-        torch.bitwise_not(src[sl], out=dst[sl])
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 4 * half * n_copy / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    copy_gbps, copy_each_way = copy_ceiling(stream, traffic_pass, copies)
 
     achieved = traffic_pass / (launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(workload),
                 "algorithmic_bytes_per_launch": traffic_pass, "kernel": KERNEL_NAME,
-                "kernel_ms": round(launch_ms, 5), "copy_ceiling_GBps": round(copy_gbps, 1)}
+                "kernel_ms": round(launch_ms, 5), "copy_ceiling_GBps": round(copy_gbps, 1),
+                "calib_copy_bytes_each_way": copy_each_way}
 
     # ---- CPU oracle baseline on this host, and bit-exactness against it:
     # whole passes over the workload's blobs until ~10 CPU-seconds are spent
@@ -254,6 +252,182 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0 if exact else 1
+
+
+def copy_ceiling(stream, traffic: int, copies: int):
+    """A plain elementwise copy kernel (torch's bitwise_not over int16: read
+    N, write N bytes) moving `traffic` bytes per launch over `copies`
+    rotated regions: the box's practical ceiling for that traffic, and the
+    known-size kernel that calibrates rocprofv3's HBM byte counters.
+    Returns (GB/s, N)."""
+    import torch
+
+    half = traffic // 4  # int16 elements: 2 bytes read + 2 written each
+    src = torch.empty(half * copies, dtype=torch.int16, device=stream.device)
+    dst = torch.empty_like(src)
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_copy = max(10, copies)
+    c0.record(stream)
+    for k in range(n_copy):
+        sl = slice((k % copies) * half, (k % copies + 1) * half)
+        torch.bitwise_not(src[sl], out=dst[sl])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return 4 * half * n_copy / (c0.elapsed_time(c1) * 1e-3) / 1e9, 2 * half
+
+
+def _time_steps(stream, fn, steps: int, warmup: int) -> float:
+    """Milliseconds per step of fn(k) over `steps` back-to-back steps, timed
+    with events on the launch stream after at least `warmup` steps and about
+    half a second of untimed work."""
+    import torch
+
+    t_warm, w = time.time(), 0
+    while True:
+        for _ in range(max(1, warmup)):
+            fn(w)
+            w += 1
+        torch.cuda.synchronize()
+        if time.time() - t_warm > 0.5:
+            break
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(steps):
+        fn(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_gemv(args, threads: int) -> int:
+    """The restore fused into its consumer: y += W x for the seven matrices of
+    one decoder layer, straight from their coded form (one launch per step).
+    Compared with the same products on the BF16 weights already restored
+    (torch.mm) and with the restore followed by those products."""
+    import torch
+
+    from lossless_bf16_weight_afx_amd import afx, synth
+
+    dev = torch.device("cuda:0")
+    m = args.m
+    specs = [sp for sp in synth.decoder_layer(0) if len(sp.shape) == 2]
+    workload = f"qwen3-14b-decoder-layer-gemv-m{m}"
+    t0 = time.time()
+    ws, blobs, infos = [], [], []
+    for sp in specs:
+        w = synth.generate(sp, threads=threads)
+        blobs.append(afx.afx_encode(w, sp.shape, threads=threads))
+        infos.append(afx.afx_query(blobs[-1]))
+        ws.append(w)
+    n_total = sum(int(i.n_elems) for i in infos)
+    blob_total = sum(int(i.blob_bytes) for i in infos)
+    x_bytes = sum(m * sp.shape[1] * 2 for sp in specs)
+    y_bytes = sum(m * sp.shape[0] * 4 for sp in specs)
+    alg = blob_total + x_bytes + 2 * y_bytes  # blobs and x read, y read and written
+    log(f"[bench] {workload}: {len(specs)} matrices, {n_total} weights, blob {blob_total} B; "
+        f"inputs ready in {time.time() - t0:.1f}s")
+
+    copies = args.copies or max(1, int(np.ceil(COLD_BYTES / blob_total)))
+    copies = min(copies, max(1, args.steps))
+    dblobs = [[torch.from_numpy(b).to(dev) for b in blobs] for _ in range(copies)]
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    xs = [torch.randn((m, sp.shape[1]), generator=gen).to(torch.bfloat16).to(dev) for sp in specs]
+    ys = [torch.zeros((m, sp.shape[0]), dtype=torch.float32, device=dev) for sp in specs]
+    jobsets = [afx.make_gemv_jobs([(i, b.data_ptr(), sp.shape[0], sp.shape[1], x.data_ptr(), y.data_ptr())
+                                   for i, b, sp, x, y in zip(infos, dblobs[c], specs, xs, ys)])
+               for c in range(copies)]
+    stream = torch.cuda.current_stream(dev)
+    sp_ = stream.cuda_stream
+
+    # ---- check (outside the timing): one launch from zero against FP32
+    # products of the bit-exact restored weights, within twice the bound
+    for y in ys:
+        y.zero_()
+    afx.afx_restore_gemv_batch_async(jobsets[0], m, sp_)
+    torch.cuda.synchronize()
+    within = True
+    for w, sp, x, y in zip(ws, specs, xs, ys):
+        wf = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16).view(*sp.shape).float()
+        xf = x.float()
+        ref = xf @ wf.t()
+        bound = (sp.shape[1] - 1) * 2.0 ** -24 * (xf.abs() @ wf.abs().t())
+        within &= bool(((y - ref).abs() <= 2 * bound + 1e-30).all())
+        del wf
+    y_fused = [y.cpu().numpy().astype(np.float64) for y in ys]
+    if not within:
+        log("[bench] fused products fall outside the FP32 summation bound")
+
+    # ---- timing of the fused launch
+    def fused(k):
+        afx.afx_restore_gemv_batch_async(jobsets[k % copies], m, sp_)
+
+    ms_fused = _time_steps(stream, fused, args.steps, args.warmup)
+    hot_ms = _time_steps(stream, lambda k: fused(0), args.steps, args.warmup)
+
+    # ---- the same products on restored BF16 weights, and restore + products
+    wbf = [[torch.empty(sp.shape, dtype=torch.bfloat16, device=dev) for sp in specs] for _ in range(copies)]
+    djobs = [afx.make_jobs([(i, b.data_ptr(), o.data_ptr(), 2 * int(i.n_elems))
+                            for i, b, o in zip(infos, dblobs[c], wbf[c])]) for c in range(copies)]
+    for c in range(copies):
+        afx.afx_decode_layer_async(djobs[c], sp_)
+
+    def mm(k):
+        for x, w in zip(xs, wbf[k % copies]):
+            torch.mm(x, w.t())
+
+    def restore_mm(k):
+        afx.afx_decode_layer_async(djobs[k % copies], sp_)
+        mm(k)
+
+    ms_mm = _time_steps(stream, mm, args.steps, args.warmup)
+    ms_rmm = _time_steps(stream, restore_mm, args.steps, args.warmup)
+    del wbf, djobs
+    copy_gbps, copy_each_way = copy_ceiling(stream, 2 * blob_total, copies)  # read and write a layer's blobs
+
+    achieved = alg / (ms_fused * 1e-3) / 1e9
+    value = 2 * n_total / (ms_fused * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(workload, "afx_gemv_kernel"),
+                "algorithmic_bytes_per_launch": alg, "kernel": "afx_gemv_kernel", "kernel_ms": round(ms_fused, 5),
+                "copy_ceiling_GBps": round(copy_gbps, 1), "calib_copy_bytes_each_way": copy_each_way}
+    compare = {"unit": "us per layer", "fused": round(ms_fused * 1e3, 1), "fused_hot_one_copy": round(hot_ms * 1e3, 1),
+               "bf16_torch_mm_on_restored": round(ms_mm * 1e3, 1),
+               "restore_then_bf16_torch_mm": round(ms_rmm * 1e3, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        for blob, sp, x, yf in zip(blobs, specs, xs, y_fused):  # also the check against the oracle
+            xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+            ref, bound = oracle.restore_gemv(blob, sp.shape[0], sp.shape[1], xb, threads=threads)
+            within &= bool((np.abs(yf - ref) <= bound).all())
+        passes, t_cpu, cpu0 = 0, 0.0, time.process_time()
+        while passes == 0 or (time.process_time() - cpu0 < 10.0 and passes < 20):
+            t1 = time.perf_counter()
+            for blob, sp, x in zip(blobs, specs, xs):
+                oracle.restore_gemv(blob, sp.shape[0], sp.shape[1], x.cpu().view(torch.int16).numpy().view(np.uint16),
+                                    threads=threads)
+            t_cpu += time.perf_counter() - t1
+            passes += 1
+        cpu = {"value": round(2 * passes * n_total / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{passes} whole passes over the layer's {len(specs)} matrices ({n_total} weights): "
+                         f"bit-serial decode on {threads} threads, float64 conversion and numpy product; "
+                         f"{time.process_time() - cpu0:.1f} CPU-s", "seconds": round(t_cpu, 2)}
+
+    line = {
+        "metric": GEMV_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_fused, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 products, f32 sums", "data": "synthetic",
+        "config": {"workload": workload, "matrices": len(specs), "weights": n_total, "m": m,
+                   "blob_bytes": blob_total, "copies": copies},
+        "within_bound": bool(within), "roofline": roofline, "compare": compare, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if within else 1
 
 
 def bench_model(args, threads: int) -> int:
