@@ -205,14 +205,27 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def restore_gemv(blob: np.ndarray, rows: int, cols: int, x_bits: np.ndarray, threads: int = 1):
-    """y = W x in float64 for the matrix W that the blob restores (row-major
-    [rows, cols]) and BF16 activations x [m, cols]; also the bound that FP32
-    summation in any order stays within: (cols - 1) * 2^-24 * sum |w x| per
-    output. The restore is this module's decoder; the product is numpy's.
+def restore_gemv(blob: np.ndarray, rows: int, cols: int, x_bits: np.ndarray, threads: int = 1, y0=None):
+    """y = y0 + W x in float64 for the matrix W that the blob restores
+    (row-major [rows, cols]), BF16 activations x [m, cols] and a starting y0
+    [m, rows] (zero when None); also the bound that FP32 summation of those
+    terms in any order stays within. Summing k values in floating point with
+    unit roundoff u, in any order, errs by at most gamma_(k-1) times the sum of
+    their magnitudes, gamma_j = j u / (1 - j u) (the classical error bound of
+    recursive and pairwise summation); here u = 2^-24, the products of two
+    BF16 values are exact in FP32, and k = cols (+ 1 with y0). The restore is
+    this module's decoder; the product is numpy's.
     Returns (y [m, rows], bound [m, rows])."""
     w = bf16_to_f64(decode(blob, threads=threads)).reshape(rows, cols)
     x = bf16_to_f64(x_bits).reshape(-1, cols)
     y = x @ w.T
-    bound = (cols - 1) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+    mag = np.abs(x) @ np.abs(w).T
+    k = cols
+    if y0 is not None:
+        y0 = np.asarray(y0, dtype=np.float64).reshape(y.shape)
+        y = y + y0
+        mag = mag + np.abs(y0)
+        k += 1
+    j = (k - 1) * 2.0 ** -24
+    bound = j / (1.0 - j) * mag
     return y, bound

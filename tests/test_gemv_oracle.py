@@ -43,6 +43,36 @@ def test_orientation_rows_times_first_column():
     assert np.array_equal(y[0], np.arange(1, rows + 1) * x0)
 
 
+def test_bound_scale_against_a_sum_that_loses_every_small_term():
+    # 1 + (cols - 1) * 2^-25 summed left to right in FP32: each 2^-25 is
+    # below half an ulp of 1 and rounds away, so the sum stays 1 and errs by
+    # (cols - 1) * 2^-25, about half the bound; a bound missing its factor
+    # (cols - 1) or off by an order of magnitude fails one of the two checks
+    rows, cols = 2, 4096
+    w = np.full(rows * cols, 0x3F80, np.uint16)  # 1.0
+    x = np.full(cols, 0x3300, np.uint16)  # 2^-25
+    x[0] = 0x3F80
+    y, bound = oracle.restore_gemv(oracle.encode(w), rows, cols, x)
+    assert np.all(y == 1 + (cols - 1) * 2.0 ** -25)
+    s = np.float32(0)
+    for v in oracle.bf16_to_f64(x).astype(np.float32):
+        s = np.float32(s + v)
+    assert s == np.float32(1.0)
+    err = abs(float(s) - y[0, 0])
+    assert err <= bound[0, 0] <= 2.5 * err
+
+
+def test_bound_with_a_starting_y():
+    rows, cols = 3, 64
+    w = np.full(rows * cols, 0x3F80, np.uint16)
+    x = bf16(np.ones(cols))
+    y0 = np.array([[1e6, -2.0, 0.0]])
+    y, bound = oracle.restore_gemv(oracle.encode(w), rows, cols, x, y0=y0)
+    assert np.array_equal(y, y0 + cols)
+    mag = np.abs(y0) + cols  # every term's magnitude, the start included
+    assert np.all(bound > mag * cols * 2.0 ** -24) and np.all(bound < mag * (cols + 1) * 2.0 ** -24)
+
+
 def test_bf16_to_f64_known_patterns():
     bits = np.array([0x3F80, 0xBF80, 0x4000, 0x0000, 0x8000, 0x3E80, 0x7F80], np.uint16)
     v = oracle.bf16_to_f64(bits)

@@ -36,10 +36,8 @@ def run(w_bits, rows, cols, m, seed, y0=None, dist="normal"):
     afx.afx_restore_gemv_async(info, dev_blob.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(),
                                torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4)
-    if y0 is not None:
-        ref = ref + y0.cpu().numpy().astype(np.float64)
-        bound = bound + np.abs(y0.cpu().numpy().astype(np.float64)) * 2.0 ** -24
+    ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4,
+                                     y0=None if y0 is None else y0.cpu().numpy())
     got = y.cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
     worst = float(np.max(err / np.maximum(bound, 1e-300)))
