@@ -180,6 +180,33 @@ typedef struct afx_gemv_job {
  * afx_restore_gemv_async. */
 int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream);
 
+/* ---- The restore fused into a product over many tokens (prefill). The
+ * same restore as above, but tiles of W go from LDS straight into the
+ * matrix cores instead of to HBM. */
+
+/* afx_restore_gemm_async: y += x W^T, where W is the tensor of the device
+ * blob (info from afx_query on a host copy), taken as row-major
+ * [rows, cols] (rows * cols == n_elems), x is BF16 [m, cols] and y FP32
+ * [m, rows], both row-major in device memory; any m >= 1. 64-row tiles of W
+ * are restored into LDS 256 columns at a time and multiplied there with
+ * BF16 matrix instructions (FP32 accumulation); tiles over different column
+ * ranges of the same rows add their partial sums into y with atomic adds,
+ * so their order (and the last bits) may differ between calls. The caller
+ * owns y and its initial contents. Enqueued on stream; returns without
+ * waiting. Errors: as afx_decode_layer_async; AFX_E_INVALID_ARG (rows *
+ * cols != n_elems, a zero size, NULL pointer), AFX_E_UNSUPPORTED (rows not
+ * a multiple of 64, cols not a multiple of 256, either >= 2^31, m == 0 or
+ * m > 8388480), AFX_E_MISALIGNED (blob or x not 16-byte aligned, y not
+ * 4-byte aligned). */
+int afx_restore_gemm_async(const afx_info *info, const void *blob_dev, uint64_t rows, uint64_t cols,
+                           const uint16_t *x_dev, uint32_t m, float *y_dev, void *stream);
+
+/* afx_restore_gemm_batch_async: afx_restore_gemm_async for every job (all
+ * with the same m), one launch per AFX_MAX_GEMV_JOBS_PER_LAUNCH jobs; all
+ * jobs are checked before anything is enqueued. Errors as
+ * afx_restore_gemm_async. */
+int afx_restore_gemm_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream);
+
 /* ---- Unpack on the host. "Why Weight Offloading Slows Inference" (section
  * "The path from storage to the GPU", Figure 1) unpacks a compressed weight
  * in RAM between the read and the copy to the GPU, and section "Lossless

@@ -29,7 +29,8 @@ AFX_READ_DIRECT = 1
 # Every symbol include/afx.h declares.
 EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_status_str",
            "afx_encode_plan", "afx_encode", "afx_file_read", "afx_decode_host",
-           "afx_restore_gemv_async", "afx_restore_gemv_batch_async")
+           "afx_restore_gemv_async", "afx_restore_gemv_batch_async", "afx_restore_gemm_async",
+           "afx_restore_gemm_batch_async")
 
 
 class AfxError(RuntimeError):
@@ -123,6 +124,10 @@ def lib() -> ctypes.CDLL:
         L.afx_restore_gemv_batch_async.argtypes = [ctypes.POINTER(afx_gemv_job), ctypes.c_size_t, ctypes.c_uint32,
                                                    ctypes.c_void_p]
         L.afx_restore_gemv_batch_async.restype = ctypes.c_int
+        L.afx_restore_gemm_async.argtypes = L.afx_restore_gemv_async.argtypes
+        L.afx_restore_gemm_async.restype = ctypes.c_int
+        L.afx_restore_gemm_batch_async.argtypes = L.afx_restore_gemv_batch_async.argtypes
+        L.afx_restore_gemm_batch_async.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -243,6 +248,23 @@ def afx_restore_gemv_batch_async(jobs, m: int, stream: int = 0) -> None:
     arr = jobs if isinstance(jobs, ctypes.Array) else make_gemv_jobs(jobs)
     _check(lib().afx_restore_gemv_batch_async(arr, len(arr), m, ctypes.c_void_p(stream)),
            "afx_restore_gemv_batch_async")
+
+
+def afx_restore_gemm_async(info: afx_info, blob_dev: int, rows: int, cols: int, x_dev: int, m: int, y_dev: int,
+                           stream: int = 0) -> None:
+    """y += x W^T with 64-row tiles of W restored into LDS for the matrix
+    cores (see afx.h)."""
+    _check(lib().afx_restore_gemm_async(ctypes.byref(info), ctypes.c_void_p(blob_dev), rows, cols,
+                                        ctypes.c_void_p(x_dev), m, ctypes.c_void_p(y_dev), ctypes.c_void_p(stream)),
+           "afx_restore_gemm_async")
+
+
+def afx_restore_gemm_batch_async(jobs, m: int, stream: int = 0) -> None:
+    """afx_restore_gemm_async for every job of a batch (array from
+    make_gemv_jobs, or tuples)."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else make_gemv_jobs(jobs)
+    _check(lib().afx_restore_gemm_batch_async(arr, len(arr), m, ctypes.c_void_p(stream)),
+           "afx_restore_gemm_batch_async")
 
 
 def afx_decode_host(blob, blob_bytes: int | None = None, out=None, threads: int = 0):

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libafx.so")
 SOURCES = [os.path.join(CSRC, "afx_host.cpp"), os.path.join(CSRC, "afx_io.cpp"),
            os.path.join(CSRC, "afx_host_decode.cpp"), os.path.join(CSRC, "afx_decode.hip"),
-           os.path.join(CSRC, "afx_gemv.hip")]
+           os.path.join(CSRC, "afx_gemv.hip"), os.path.join(CSRC, "afx_gemm.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 instructions are kept out of every device build.

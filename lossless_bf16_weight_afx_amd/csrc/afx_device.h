@@ -70,11 +70,14 @@ __device__ inline void wave_sync() {
 // the stream, MSB first) holds (symbol << 8) | length of the code word that
 // starts the window. The length sits in the low bits so that a 32-bit shift
 // by the whole entry consumes exactly the code (the hardware reads only the
-// low 5 bits of a shift amount). All 1024 threads take part: thread s < 256
-// owns symbol s and passes its code length (the others pass 0), then every
-// thread s fills table entries [4 s, 4 s + 4). Callers bracket it with
+// low 5 bits of a shift amount). All kNThreads threads of the workgroup
+// (256 or more) take part: thread s < 256 owns symbol s and passes its code
+// length (the others pass 0), then every thread s fills table entries
+// [kPer s, kPer s + kPer), kPer = 4096 / kNThreads. Callers bracket it with
 // barriers.
+template <int kNThreads = kThreads>
 __device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
+    static_assert(kNThreads >= 256 && kLutEntries % (4 * kNThreads) == 0, "4-entry blocks per thread");
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1), wave = s / kWave;
     uint32_t rank = 0;  // among same-length symbols of this wave with smaller value
@@ -133,15 +136,22 @@ __device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
         const uint32_t j = S.base[l] + (idx >> (kMaxLen - l));
         return ((uint32_t)S.sorted[j & 255] << 8) | l;
     };
-    constexpr uint32_t kPer = kLutEntries / kThreads;  // 4 entries per thread
-    const uint32_t i0 = (uint32_t)s * kPer;
-    const uint32_t e0 = entry(i0);
-    if ((e0 & 0xFF) <= kMaxLen - 2) {
-        // a code of <= 10 bits owns whole 4-aligned blocks of the index space
-        const uint32_t d = e0 | (e0 << 16);
-        *reinterpret_cast<uint2 *>(lut + i0) = make_uint2(d, d);
+    constexpr uint32_t kPer = kLutEntries / kNThreads;  // entries per thread
+    // a code of <= 10 bits owns whole 4-aligned blocks of the index space
+    auto fill4 = [&](uint32_t i0) {
+        const uint32_t e0 = entry(i0);
+        if ((e0 & 0xFF) <= kMaxLen - 2) {
+            const uint32_t d = e0 | (e0 << 16);
+            *reinterpret_cast<uint2 *>(lut + i0) = make_uint2(d, d);
+        } else {
+            for (uint32_t j = 0; j < 4; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
+        }
+    };
+    if constexpr (kPer == 4) {
+        fill4((uint32_t)s * 4);
     } else {
-        for (uint32_t j = 0; j < kPer; ++j) lut[i0 + j] = (uint16_t)entry(i0 + j);
+#pragma unroll
+        for (uint32_t b = 0; b < kPer; b += 4) fill4((uint32_t)s * kPer + b);
     }
 }
 

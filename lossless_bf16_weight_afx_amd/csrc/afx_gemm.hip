@@ -1,0 +1,361 @@
+// afx_gemm.hip -- the restore fused into a matrix product on the matrix cores
+// (gfx950): Y += X W^T for a weight matrix W held only in its coded form.
+//
+// "Why Weight Offloading Slows Inference" (section "Lossless compression")
+// restores the released bits of a compressed weight before computation. For a
+// product over many tokens at once (a prompt), restoring W into HBM first
+// writes and rereads 2 bytes per weight; here tiles of W are restored into
+// LDS and consumed there by MFMA, and only the coded matrix is read from HBM.
+//
+// W is row-major [rows, cols] (the blob's element order), X is BF16 [m, cols]
+// and Y is FP32 [m, rows], both row-major: Y[t, r] += sum_k X[t, k] W[r, k].
+//
+// Work decomposition:
+//   * a tile is 64 rows of W by a range of up to 2560 columns; a workgroup of
+//     4 wave64s takes one tile and up to 128 tokens (blockIdx.y picks the
+//     token block). Every tile adds its partial sums into Y with atomic adds,
+//     so ranges of one row may run on different workgroups;
+//   * the tile's columns are restored 256 at a time (a slab of 64 x 256
+//     values). A 32-element group decodes on its own from its chunk's bit
+//     base and its gap, so a slab is 64 x 8 groups: wave w restores rows
+//     16w..16w+15, one quad of lanes per row, two groups per lane. The row's
+//     code words for the slab (one contiguous bit range) are staged in LDS by
+//     its quad; each lane then runs its two groups' table-driven chains;
+//   * the restored slab goes to LDS in row-major order (rows padded by 16
+//     bytes), where it is the B operand of v_mfma_f32_32x32x16_bf16: wave w
+//     multiplies tokens 32w..32w+31 (X read from L2 straight into the A
+//     operand) with the slab's two 32-row halves.
+// Lane layout of v_mfma_f32_32x32x16_bf16: lane l holds A[l % 32][8 (l / 32)
+// + 0..7] and B[8 (l / 32) + 0..7][l % 32]; accumulator v of lane l is
+// D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+#include <hip/hip_runtime.h>
+
+#include "afx_device.h"
+
+namespace afx {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmWaves = 4;
+constexpr int kGemmThreads = kGemmWaves * kWave;             // 256
+constexpr uint32_t kTileRows = 64;                           // W rows per tile (two MFMA N blocks)
+constexpr uint32_t kSlabCols = 256;                          // columns restored per step
+constexpr uint32_t kRangeSlabs = 10;                         // a tile spans <= 2560 columns
+constexpr uint32_t kRangeCols = kRangeSlabs * kSlabCols;
+constexpr uint32_t kTileTokens = 32 * kGemmWaves;            // 128 tokens per workgroup
+constexpr uint32_t kRowsPerWave = kTileRows / kGemmWaves;    // 16
+// Code words staged per row segment: 256 codes of <= 12 bits (96 words), the
+// 16-byte alignment of the first word (3), the bit offset inside it and one
+// word of look-ahead for the last two-code window (2), rounded to 16 bytes.
+constexpr uint32_t kSegWords = 104;
+constexpr uint32_t kSlabStride = kSlabCols * 2 + 16;         // bytes per restored row in LDS
+
+struct GemmJob {
+    TensorDesc t;        // t.out, t.blk_* unused
+    const uint16_t *x;   // BF16 [m, cols]
+    float *y;            // FP32 [m, rows], added into
+    uint32_t rows, cols;
+    uint32_t tile0;      // first tile of this job in the grid
+    uint32_t n_rtiles;   // rows / 64
+};
+
+struct GemmBatch {
+    GemmJob j[AFX_MAX_GEMV_JOBS_PER_LAUNCH];
+    uint32_t n;
+    uint32_t m;
+};
+
+// 16 bytes of x as the A operand (zeros for a token beyond m).
+__device__ inline bf16x8 load_a(const uint16_t *p, bool ok) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok) v = *reinterpret_cast<const uint4 *>(p);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// The 32 stream bits at bit offset P of a staged row segment, MSB first.
+__device__ inline uint32_t seg_window(const uint32_t *seg, uint32_t P) {
+    const uint32_t i = min(P >> 5, kSegWords - 2);  // a corrupt stream stays inside the segment
+    const uint64_t two = ((uint64_t)seg[i] << 32) | seg[i + 1];
+    return (uint32_t)(two >> (32 - (P & 31)));
+}
+
+// Decode the 32 exponent codes of one group from bit offset P of its row's
+// staged segment; ex[j] receives the exponent bytes of elements 4j..4j+3.
+__device__ inline void decode_group(const uint32_t *seg, uint32_t P, const uint16_t *lut, uint32_t (&ex)[8]) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {  // two codes (<= 24 bits) per 32-bit window
+        const uint32_t w = seg_window(seg, P);
+        const uint32_t e1 = lut[w >> (32 - kMaxLen)];
+        const uint32_t e2 = lut[(w << (e1 & 31)) >> (32 - kMaxLen)];
+        P += (e1 & 0xFF) + (e2 & 0xFF);
+        const uint32_t pair = (e1 >> 8) | (e2 & 0xFF00);
+        if (t & 1) ex[t >> 1] |= pair << 16;
+        else ex[t >> 1] = pair;
+    }
+}
+
+
+__device__ inline uint64_t quad_first(uint64_t v) {  // every lane gets lane 4 (l / 4)'s value
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x00, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), 0x00, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// What the bit offsets of a row segment (starting at element e_seg) are
+// made of: chunk base and gap of the lane's two groups (q4 and q4 + 4 of the
+// segment's 8) and of the group after the segment (at the end of the
+// tensor: the stream's end, with gap 0). Kept as loaded and added up only
+// where used, so that issuing them never waits for them.
+struct SlabBits {
+    uint64_t b1, b2, be;
+    uint32_t g1, g2, ge;
+    bool last;  // the segment ends the tensor
+};
+__device__ inline SlabBits slab_bits(const TensorDesc &T, uint64_t e_seg, uint32_t q4) {
+    SlabBits b;
+    const uint64_t e1 = e_seg + kGroup * q4, e2 = e1 + kGroup * 4, e_end = e_seg + kSlabCols;
+    b.last = e_end >= T.n;
+    b.b1 = T.chunk_base[e1 >> 12];
+    b.g1 = T.gap[e1 >> 5];
+    b.b2 = T.chunk_base[e2 >> 12];
+    b.g2 = T.gap[e2 >> 5];
+    b.be = T.chunk_base[b.last ? T.n_chunks : e_end >> 12];
+    b.ge = T.gap[b.last ? 0 : e_end >> 5];
+    return b;
+}
+__device__ inline uint64_t bit1(const SlabBits &b) { return b.b1 + b.g1; }
+__device__ inline uint64_t bit2(const SlabBits &b) { return b.b2 + b.g2; }
+__device__ inline uint64_t bit_end(const SlabBits &b) { return b.be + (b.last ? 0u : b.ge); }
+
+// The segment's staged word range [wa, wa + nw) (16-byte aligned), the
+// first 32 of those words (lane q4 of the quad holds words 4 q4.. and
+// 16 + 4 q4..), and the sign/mantissa bytes of the lane's two groups.
+struct SlabData {
+    uint64_t wa;
+    uint32_t nw;
+    uint4 w0, w1;
+    u32x4 s1a, s1b, s2a, s2b;
+};
+__device__ inline SlabData slab_data(const TensorDesc &T, uint64_t e_seg, uint32_t q4, const SlabBits &b) {
+    SlabData d;
+    const uint64_t p_lo = quad_first(bit1(b)), p_hi = bit_end(b);
+    d.wa = (p_lo >> 5) & ~3ull;
+    const uint64_t need = p_hi >= p_lo ? ((p_hi + 31) >> 5) + 1 - d.wa : 0;  // corrupt: stage nothing
+    d.nw = (uint32_t)umin64(need, kSegWords);
+    // (words past the segment's end are staged too, and never read)
+    d.w0 = load_words4(T, d.wa + 4 * q4);
+    d.w1 = load_words4(T, d.wa + 16 + 4 * q4);
+    // sign/mantissa bytes are read once: keep them out of the caches
+    const u32x4 *sm1 = reinterpret_cast<const u32x4 *>(T.signmant + e_seg + kGroup * q4);
+    const u32x4 *sm2 = reinterpret_cast<const u32x4 *>(T.signmant + e_seg + kGroup * (q4 + 4));
+    d.s1a = __builtin_nontemporal_load(sm1);
+    d.s1b = __builtin_nontemporal_load(sm1 + 1);
+    d.s2a = __builtin_nontemporal_load(sm2);
+    d.s2b = __builtin_nontemporal_load(sm2 + 1);
+    return d;
+}
+
+__global__ __launch_bounds__(kGemmThreads, 2)
+void afx_gemm_kernel(const GemmBatch batch) {
+    __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];                  // 8 KB
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kTileRows * kSegWords];       // 26 KB
+    __shared__ __attribute__((aligned(16))) uint8_t slab[kTileRows * kSlabStride];       // 33 KB
+    __shared__ LutScratch scratch;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    uint32_t jb = 0;
+    for (uint32_t i = 1; i < batch.n; ++i)
+        if (blockIdx.x >= batch.j[i].tile0) jb = i;
+    const GemmJob &J = batch.j[jb];
+    const TensorDesc &T = J.t;
+    const uint32_t tile = blockIdx.x - J.tile0;
+    const uint32_t r0 = (tile % J.n_rtiles) * kTileRows;
+    const uint32_t kbeg = (tile / J.n_rtiles) * kRangeCols;
+    const uint32_t kend = min(J.cols, kbeg + kRangeCols);
+    const uint32_t t0 = blockIdx.y * kTileTokens;
+    const uint32_t m = batch.m;
+
+    build_lut<kGemmThreads>(T.code_len[threadIdx.x], lut, scratch);
+    __syncthreads();
+
+    // Restore: this lane's row (one quad per row) and its two groups.
+    const uint32_t q4 = (uint32_t)lane & 3;
+    const uint32_t row = wave * kRowsPerWave + ((uint32_t)lane >> 2);  // tile-local
+    const uint64_t row_e = (uint64_t)(r0 + row) * J.cols;              // element of W[r0 + row, 0]
+    uint32_t *seg = stage + row * kSegWords;
+    uint8_t *out_row = slab + row * kSlabStride;
+    // Multiply: this lane's token (A row) and the wave's token block.
+    const uint32_t tok = t0 + wave * 32 + ((uint32_t)lane & 31);
+    const bool tok_ok = tok < m;
+    const bool wave_mul = t0 + wave * 32 < m;
+    const uint16_t *xa_p = J.x + (uint64_t)(tok_ok ? tok : 0) * J.cols + 8 * ((uint32_t)lane >> 5);
+    const uint8_t *b_row0 = slab + ((uint32_t)lane & 31) * kSlabStride + 16 * ((uint32_t)lane >> 5);
+    const uint8_t *b_row1 = b_row0 + 32 * kSlabStride;
+
+    // Software pipeline over the slabs: while slab s is restored and
+    // multiplied, the code words and sign/mantissa bytes of slab s + 1 and
+    // the group bit offsets of slab s + 2 are in flight, so that the two
+    // dependent round trips (offsets, then the words they point at) stay off
+    // the path of every slab but the first.
+    SlabBits bits_c = slab_bits(T, row_e + kbeg, q4);
+    SlabData data_c = slab_data(T, row_e + kbeg, q4, bits_c);
+    const bool two = kbeg + kSlabCols < kend;
+    SlabBits bits_n = two ? slab_bits(T, row_e + kbeg + kSlabCols, q4) : bits_c;
+    f32x16 acc0 = {}, acc1 = {};
+    for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
+        const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
+        // Stage this slab's code words (loaded a slab ago; a segment longer
+        // than the prefetched 32 words loads the rest now).
+        *reinterpret_cast<uint4 *>(seg + 4 * q4) = data_c.w0;
+        *reinterpret_cast<uint4 *>(seg + 16 + 4 * q4) = data_c.w1;
+        for (uint32_t i = 32 + 4 * q4; i < data_c.nw; i += 16)
+            *reinterpret_cast<uint4 *>(seg + i) = load_words4(T, data_c.wa + i);
+        // Issue the next slabs' loads, then this slab's A operands.
+        SlabData data_n = data_c;
+        if (has_n) data_n = slab_data(T, row_e + k0 + kSlabCols, q4, bits_n);
+        SlabBits bits_nn = bits_n;
+        if (has_nn) bits_nn = slab_bits(T, row_e + k0 + 2 * kSlabCols, q4);
+        bf16x8 xa[kSlabCols / 16];
+        if (wave_mul) {
+#pragma unroll
+            for (uint32_t ks = 0; ks < kSlabCols / 16; ++ks) xa[ks] = load_a(xa_p + k0 + 16 * ks, tok_ok);
+        }
+        wave_sync();
+        uint32_t ex1[8], ex2[8];
+        decode_group(seg, (uint32_t)umin64(bit1(bits_c) - 32 * data_c.wa, 32 * (kSegWords - 2)), lut, ex1);
+        decode_group(seg, (uint32_t)umin64(bit2(bits_c) - 32 * data_c.wa, 32 * (kSegWords - 2)), lut, ex2);
+        // Join and put both groups into the slab.
+        const uint32_t b1[8] = {data_c.s1a.x, data_c.s1a.y, data_c.s1a.z, data_c.s1a.w,
+                                data_c.s1b.x, data_c.s1b.y, data_c.s1b.z, data_c.s1b.w};
+        const uint32_t b2[8] = {data_c.s2a.x, data_c.s2a.y, data_c.s2a.z, data_c.s2a.w,
+                                data_c.s2b.x, data_c.s2b.y, data_c.s2b.z, data_c.s2b.w};
+        uint4 *o1 = reinterpret_cast<uint4 *>(out_row + 64 * q4);
+        uint4 *o2 = reinterpret_cast<uint4 *>(out_row + 64 * (q4 + 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o1[j] = make_uint4(join_pair<false>(b1[2 * j], ex1[2 * j]), join_pair<true>(b1[2 * j], ex1[2 * j]),
+                               join_pair<false>(b1[2 * j + 1], ex1[2 * j + 1]),
+                               join_pair<true>(b1[2 * j + 1], ex1[2 * j + 1]));
+            o2[j] = make_uint4(join_pair<false>(b2[2 * j], ex2[2 * j]), join_pair<true>(b2[2 * j], ex2[2 * j]),
+                               join_pair<false>(b2[2 * j + 1], ex2[2 * j + 1]),
+                               join_pair<true>(b2[2 * j + 1], ex2[2 * j + 1]));
+        }
+        __syncthreads();  // the slab is complete
+        if (wave_mul) {
+#pragma unroll
+            for (uint32_t ks = 0; ks < kSlabCols / 16; ++ks) {
+                const bf16x8 w0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row0 + 32 * ks));
+                const bf16x8 w1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row1 + 32 * ks));
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks], w0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks], w1, acc1, 0, 0, 0);
+            }
+        }
+        __syncthreads();  // every wave is done with the slab and its staged words
+        bits_c = bits_n;
+        bits_n = bits_nn;
+        data_c = data_n;
+    }
+    if (!wave_mul) return;
+    const uint32_t col = r0 + ((uint32_t)lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const uint32_t t = t0 + wave * 32 + 8 * (v / 4) + 4 * ((uint32_t)lane >> 5) + (v & 3);
+        if (t < m) {
+            float *yr = J.y + (uint64_t)t * J.rows;
+            atomicAdd(yr + col, acc0[v]);
+            atomicAdd(yr + col + 32, acc1[v]);
+        }
+    }
+}
+
+}  // namespace
+
+int check_gemm_job(const afx_gemv_job &j, uint32_t m) {
+    int rc = check_info(j.info);
+    if (rc != AFX_OK) return rc;
+    if (!j.blob_dev || !j.x_dev || !j.y_dev || j.rows == 0 || j.cols == 0) return AFX_E_INVALID_ARG;
+    if (j.rows * j.cols != j.info->n_elems || j.info->n_elems / j.cols != j.rows) return AFX_E_INVALID_ARG;
+    if (m == 0 || m > 65535u * kTileTokens) return AFX_E_UNSUPPORTED;
+    if (j.rows % kTileRows || j.cols % kSlabCols || j.rows >= (1ull << 31) || j.cols >= (1ull << 31))
+        return AFX_E_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(j.blob_dev) & 15) || (reinterpret_cast<uintptr_t>(j.x_dev) & 15) ||
+        (reinterpret_cast<uintptr_t>(j.y_dev) & 3))
+        return AFX_E_MISALIGNED;
+    return AFX_OK;
+}
+
+namespace {
+
+GemmJob gemm_job(const afx_gemv_job &j) {
+    const afx_info *info = j.info;
+    const uint8_t *b = static_cast<const uint8_t *>(j.blob_dev);
+    GemmJob g{};
+    g.t.code_len = b + info->off_code_len;
+    g.t.chunk_base = reinterpret_cast<const uint64_t *>(b + info->off_chunk_base);
+    g.t.gap = reinterpret_cast<const uint16_t *>(b + info->off_gap);
+    g.t.signmant = b + info->off_signmant;
+    g.t.exp = reinterpret_cast<const uint32_t *>(b + info->off_exp);
+    g.t.out = nullptr;
+    g.t.n = info->n_elems;
+    g.t.exp_words = info->exp_words;
+    g.t.last_word4 = (info->exp_words - 4) & ~(uint64_t)3;
+    g.t.n_chunks = (uint32_t)info->n_chunks;
+    g.x = j.x_dev;
+    g.y = j.y_dev;
+    g.rows = (uint32_t)j.rows;
+    g.cols = (uint32_t)j.cols;
+    g.n_rtiles = (uint32_t)(j.rows / kTileRows);
+    return g;
+}
+
+int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t stream) {
+    GemmBatch batch{};
+    batch.m = m;
+    uint64_t tiles = 0;
+    for (size_t i = 0; i < n_jobs; ++i) {
+        GemmJob g = gemm_job(jobs[i]);
+        g.tile0 = (uint32_t)tiles;
+        tiles += (uint64_t)g.n_rtiles * ((g.cols + kRangeCols - 1) / kRangeCols);
+        batch.j[batch.n++] = g;
+    }
+    if (tiles == 0) return AFX_OK;
+    if (tiles >= (1ull << 31)) return AFX_E_UNSUPPORTED;
+    const uint32_t tok_blocks = (m + kTileTokens - 1) / kTileTokens;
+    hipLaunchKernelGGL(afx_gemm_kernel, dim3((unsigned)tiles, tok_blocks), dim3(kGemmThreads), 0, stream, batch);
+    return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
+}
+
+}  // namespace
+}  // namespace afx
+
+using namespace afx;
+
+extern "C" {
+
+int afx_restore_gemm_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream) {
+    if (!jobs && n_jobs) return AFX_E_INVALID_ARG;
+    for (size_t i = 0; i < n_jobs; ++i) {
+        const int rc = check_gemm_job(jobs[i], m);
+        if (rc != AFX_OK) return rc;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (size_t i = 0; i < n_jobs; i += AFX_MAX_GEMV_JOBS_PER_LAUNCH) {
+        const size_t k = std::min<size_t>(AFX_MAX_GEMV_JOBS_PER_LAUNCH, n_jobs - i);
+        const int rc = launch_gemm(jobs + i, k, m, s);
+        if (rc != AFX_OK) return rc;
+    }
+    return AFX_OK;
+}
+
+int afx_restore_gemm_async(const afx_info *info, const void *blob_dev, uint64_t rows, uint64_t cols,
+                           const uint16_t *x_dev, uint32_t m, float *y_dev, void *stream) {
+    const afx_gemv_job job{info, blob_dev, rows, cols, x_dev, y_dev};
+    return afx_restore_gemm_batch_async(&job, 1, m, stream);
+}
+
+}  // extern "C"

@@ -103,3 +103,27 @@ def test_entry_point_argument_errors():
     assert rc(64, 4096, xp=fake + 8) == afx.AFX_E_MISALIGNED
     assert rc(64, 4096, y=fake + 2) == afx.AFX_E_MISALIGNED
     assert rc(64, 4096, blob=fake + 4) == afx.AFX_E_MISALIGNED
+
+
+def test_gemm_entry_point_argument_errors():
+    afx.lib()
+    x = synth.generate(synth.TensorSpec("t", (128, 512), "normal", 4))
+    info = afx.afx_query(oracle.encode(x, (128, 512)))
+    fake = 1 << 40  # never dereferenced: every check below precedes any HIP call
+    def rc(rows, cols, m=1, blob=fake, xp=fake, y=fake):
+        try:
+            afx.afx_restore_gemm_async(info, blob, rows, cols, xp, m, y, 0)
+        except afx.AfxError as e:
+            return e.status
+        return afx.AFX_OK
+    assert rc(128, 511) == afx.AFX_E_INVALID_ARG
+    assert rc(0, 512) == afx.AFX_E_INVALID_ARG
+    assert rc(512, 128) == afx.AFX_E_UNSUPPORTED  # cols not a multiple of 256
+    assert rc(32, 2048) == afx.AFX_E_UNSUPPORTED  # rows not a multiple of 64
+    assert rc(128, 512, m=0) == afx.AFX_E_UNSUPPORTED
+    assert rc(128, 512, blob=0) == afx.AFX_E_INVALID_ARG
+    assert rc(128, 512, xp=0) == afx.AFX_E_INVALID_ARG
+    assert rc(128, 512, y=0) == afx.AFX_E_INVALID_ARG
+    assert rc(128, 512, xp=fake + 8) == afx.AFX_E_MISALIGNED
+    assert rc(128, 512, y=fake + 2) == afx.AFX_E_MISALIGNED
+    assert rc(128, 512, blob=fake + 4) == afx.AFX_E_MISALIGNED

@@ -1,0 +1,133 @@
+"""GPU parity of the restore fused into a matrix product on the matrix cores:
+y += x W^T with 64-row tiles of W restored into LDS, against the oracle's
+float64 product of the restored matrix.
+
+Small-integer weights and activations keep every partial sum exact in FP32,
+so there the result must equal the oracle's exactly, whatever the order of
+the sums: any indexing mistake (a transposed tile, a wrong slab, a lane
+layout) shows. Other data are checked within twice the classical bound of
+FP32 summation, gamma_(k-1) * sum |terms| (the matrix instructions' internal
+rounding is not documented; twice the bound allows one unit in the last place
+per addition instead of half of one)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_bf16_weight_afx_amd import afx, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    afx.lib()
+
+
+def gemm(blob, rows, cols, x_bits, m, y0=None):
+    info = afx.afx_query(blob)
+    db = afx.to_device(blob)
+    xd = torch.from_numpy(x_bits.view(np.int16)).to("cuda")
+    y = torch.zeros((m, rows), dtype=torch.float32, device="cuda") if y0 is None else y0.clone()
+    afx.afx_restore_gemm_async(info, db.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def small_ints(rng, shape, lo, hi):
+    return synth.f32_to_bf16_bits(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("rows,cols,m", [
+    (64, 256, 1),       # one tile, one slab, one token
+    (128, 768, 37),     # two row tiles, three slabs, a partial token block
+    (192, 2816, 130),   # two column ranges (2560 + 256), two token blocks
+    (64, 17408, 64),    # down_proj-shaped rows: seven column ranges
+])
+def test_integer_data_exact(rows, cols, m):
+    say(f"[gpu] case gemm integers {rows}x{cols} m={m}")
+    rng = np.random.default_rng(rows + cols + m)
+    w = small_ints(rng, rows * cols, -3, 3)
+    x = small_ints(rng, (m, cols), -2, 2)
+    blob = oracle.encode(w, (rows, cols))
+    got = gemm(blob, rows, cols, x, m)
+    ref, _ = oracle.restore_gemv(blob, rows, cols, x, threads=4)
+    assert np.abs(ref).max() < 2 ** 24  # every partial sum is exact in FP32
+    assert np.array_equal(got, ref)
+
+
+def check(blob, rows, cols, x, m, y0=None):
+    got = gemm(blob, rows, cols, x, m, y0)
+    ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4,
+                                     y0=None if y0 is None else y0.cpu().numpy())
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(2 * bound, 1e-300)))
+    assert np.all(err <= 2 * bound), f"error above twice the bound: worst ratio {worst}"
+    return worst
+
+
+@pytest.mark.parametrize("rows,cols,m,dist", [
+    (64, 5120, 128, "normal"),     # a q_proj-shaped row tile, one full token block
+    (320, 5120, 200, "normal"),
+    (128, 17408, 16, "normal"),
+    (256, 5120, 33, "t4"),         # heavy tails: longer codes
+])
+def test_random_data_within_bound(rows, cols, m, dist):
+    say(f"[gpu] case gemm {dist} {rows}x{cols} m={m}")
+    w = synth.generate(synth.TensorSpec("w", (rows, cols), dist, rows + cols + m))
+    x = synth.f32_to_bf16_bits(np.random.default_rng(m).standard_normal((m, cols)).astype(np.float32))
+    worst = check(oracle.encode(w, (rows, cols)), rows, cols, x, m)
+    say(f"[gpu]   worst error / (2 bound) = {worst:.3g}")
+
+
+def test_twelve_bit_codes_and_a_starting_y():
+    """Exponents spread over all 256 values: codes up to the 12-bit limit and
+    the longest staged row segments; y starts from nonzero values."""
+    say("[gpu] case gemm 256 exponent values, y accumulated onto existing values")
+    rows, cols, m = 128, 1024, 40
+    rng = np.random.default_rng(12)
+    e = np.minimum(rng.geometric(0.02, size=rows * cols), 255).astype(np.uint16)
+    w = (rng.integers(0, 2, rows * cols).astype(np.uint16) << 15) | (e << 7) | rng.integers(0, 128, rows * cols).astype(np.uint16)
+    w[(e == 255)] &= 0x807F  # keep them finite: no Inf or NaN in the products
+    w[(e == 255)] |= 254 << 7
+    blob = oracle.encode(w, (rows, cols))
+    assert afx.afx_query(blob).longest_code == 12
+    x = synth.f32_to_bf16_bits((rng.standard_normal((m, cols)) * 1e-30).astype(np.float32))
+    y0 = torch.randn((m, rows), dtype=torch.float32, device="cuda")
+    check(blob, rows, cols, x, m, y0)
+
+
+def test_layer_batch_one_launch():
+    """The seven matrices of one Qwen3-14B-shaped decoder layer in one batch
+    call at m = 16; every product within its bound."""
+    m = 16
+    specs = [s for s in synth.decoder_layer(0) if len(s.shape) == 2]
+    rng = np.random.default_rng(41)
+    jobs, keep = [], []
+    for sp in specs:
+        rows, cols = sp.shape
+        blob = afx.afx_encode(synth.generate(sp, threads=16), sp.shape, threads=16)
+        info = afx.afx_query(blob)
+        db = afx.to_device(blob)
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, cols)).astype(np.float32))
+        xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+        y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+        keep.append((blob, x, y, db, xd, info))
+        jobs.append((info, db.data_ptr(), rows, cols, xd.data_ptr(), y.data_ptr()))
+    say("[gpu] case gemm batch of a layer's 7 matrices, m=16")
+    afx.afx_restore_gemm_batch_async(jobs, m, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for (blob, x, y, _, _, _), sp in zip(keep, specs):
+        ref, bound = oracle.restore_gemv(blob, sp.shape[0], sp.shape[1], x, threads=16)
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= 2 * bound), sp.name

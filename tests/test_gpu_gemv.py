@@ -1,7 +1,7 @@
 """GPU parity of the restore fused into a matrix-vector product: y += W x with
 W restored on the fly, against the oracle's float64 product of the restored
 matrix, within the bound that FP32 summation in any order keeps:
-(cols - 1) * 2^-24 * sum |w x| per output."""
+gamma_(cols-1) * sum |w x| per output, gamma_j = j u / (1 - j u), u = 2^-24."""
 import sys
 
 import numpy as np
