@@ -277,8 +277,13 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
         batch.t[t].blk_lo = (uint32_t)lo;
         batch.t[t].blk_hi = (uint32_t)hi;
     }
-    hipLaunchKernelGGL(afx_decode_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, batch);
-    return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
+    // hipLaunchKernel reports this launch's own status (an error left pending
+    // by an earlier, unrelated HIP call is not mistaken for it)
+    void *args[] = {&batch};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&afx_decode_kernel), dim3((unsigned)grid), dim3(kThreads),
+                           args, 0, stream) == hipSuccess
+               ? AFX_OK
+               : AFX_E_HIP;
 }
 
 }  // namespace

@@ -49,7 +49,13 @@ constexpr uint32_t kRowsPerWave = kTileRows / kGemmWaves;    // 16
 // Code words staged per row segment: 256 codes of <= 12 bits (96 words), the
 // 16-byte alignment of the first word (3), the bit offset inside it and one
 // word of look-ahead for the last two-code window (2), rounded to 16 bytes.
+// They are staged in reverse order (stream word wa + i at index kSegRev - i),
+// so that the decoding chains of afx_device.h apply; a row's slice has one
+// more word above kSegRev for their reads.
 constexpr uint32_t kSegWords = 104;
+constexpr uint32_t kSegRev = kSegWords - 1;                  // == 3 (mod 4): aligned reversed stores
+constexpr uint32_t kSegRow = kSegWords + 4;                  // words per row slice
+static_assert(kSegRev % 4 == 3, "reversed staging needs kSegRev = 3 mod 4");
 constexpr uint32_t kSlabStride = kSlabCols * 2 + 16;         // bytes per restored row in LDS
 
 struct GemmJob {
@@ -74,28 +80,31 @@ __device__ inline bf16x8 load_a(const uint16_t *p, bool ok) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// The 32 stream bits at bit offset P of a staged row segment, MSB first.
-__device__ inline uint32_t seg_window(const uint32_t *seg, uint32_t P) {
-    const uint32_t i = min(P >> 5, kSegWords - 2);  // a corrupt stream stays inside the segment
-    const uint64_t two = ((uint64_t)seg[i] << 32) | seg[i + 1];
-    return (uint32_t)(two >> (32 - (P & 31)));
+// Stage four stream words (those at wa + i .. wa + i + 3) of a row segment,
+// reversed: stream word wa + j goes to index kSegRev - j.
+__device__ inline void put_seg4(uint32_t *seg, uint32_t i, uint4 v) {
+    *reinterpret_cast<uint4 *>(seg + (kSegRev - 3 - i)) = make_uint4(v.w, v.z, v.y, v.x);
 }
 
-// Decode the 32 exponent codes of one group from bit offset P of its row's
-// staged segment; ex[j] receives the exponent bytes of elements 4j..4j+3.
-__device__ inline void decode_group(const uint32_t *seg, uint32_t P, const uint16_t *lut, uint32_t (&ex)[8]) {
+// Decode the 32 exponent codes of the lane's two groups, which start at bit
+// offsets P1 and P2 of the row's staged segment (two interleaved buffered
+// chains); ex1[j], ex2[j] receive the exponent bytes of elements 4j..4j+3.
+// A chain start stays low enough that 32 codes of <= 12 bits, and the
+// chains' read-ahead, remain inside the slice even on a corrupt stream.
+__device__ inline void decode_groups(const uint32_t *seg, uint32_t P1, uint32_t P2, const uint16_t *lut,
+                                     uint32_t (&ex1)[8], uint32_t (&ex2)[8]) {
+    constexpr uint32_t kMaxStart = 32 * (kSegRev - 13);
+    BufChain A = buf_chain(seg, 32 * kSegRev - min(P1, kMaxStart));
+    BufChain B = buf_chain(seg, 32 * kSegRev - min(P2, kMaxStart));
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {  // two codes (<= 24 bits) per 32-bit window
-        const uint32_t w = seg_window(seg, P);
-        const uint32_t e1 = lut[w >> (32 - kMaxLen)];
-        const uint32_t e2 = lut[(w << (e1 & 31)) >> (32 - kMaxLen)];
-        P += (e1 & 0xFF) + (e2 & 0xFF);
-        const uint32_t pair = (e1 >> 8) | (e2 & 0xFF00);
-        if (t & 1) ex[t >> 1] |= pair << 16;
-        else ex[t >> 1] = pair;
+    for (int q = 0; q < 8; ++q) {
+        uint32_t a01, b01, a23, b23;
+        buf_chain_pairs(A, B, seg, lut, a01, b01);
+        buf_chain_pairs(A, B, seg, lut, a23, b23);
+        ex1[q] = join_halves(a01, a23);
+        ex2[q] = join_halves(b01, b23);
     }
 }
-
 
 __device__ inline uint64_t quad_first(uint64_t v) {  // every lane gets lane 4 (l / 4)'s value
     const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x00, 0xF, 0xF, false);
@@ -162,7 +171,7 @@ __device__ inline SlabData slab_data(const TensorDesc &T, uint64_t e_seg, uint32
 __global__ __launch_bounds__(kGemmThreads, 2)
 void afx_gemm_kernel(const GemmBatch batch) {
     __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];                  // 8 KB
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kTileRows * kSegWords];       // 26 KB
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kTileRows * kSegRow];         // 27 KB
     __shared__ __attribute__((aligned(16))) uint8_t slab[kTileRows * kSlabStride];       // 33 KB
     __shared__ LutScratch scratch;
 
@@ -187,7 +196,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t q4 = (uint32_t)lane & 3;
     const uint32_t row = wave * kRowsPerWave + ((uint32_t)lane >> 2);  // tile-local
     const uint64_t row_e = (uint64_t)(r0 + row) * J.cols;              // element of W[r0 + row, 0]
-    uint32_t *seg = stage + row * kSegWords;
+    uint32_t *seg = stage + row * kSegRow;
     uint8_t *out_row = slab + row * kSlabStride;
     // Multiply: this lane's token (A row) and the wave's token block.
     const uint32_t tok = t0 + wave * 32 + ((uint32_t)lane & 31);
@@ -211,10 +220,9 @@ void afx_gemm_kernel(const GemmBatch batch) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
         // than the prefetched 32 words loads the rest now).
-        *reinterpret_cast<uint4 *>(seg + 4 * q4) = data_c.w0;
-        *reinterpret_cast<uint4 *>(seg + 16 + 4 * q4) = data_c.w1;
-        for (uint32_t i = 32 + 4 * q4; i < data_c.nw; i += 16)
-            *reinterpret_cast<uint4 *>(seg + i) = load_words4(T, data_c.wa + i);
+        put_seg4(seg, 4 * q4, data_c.w0);
+        put_seg4(seg, 16 + 4 * q4, data_c.w1);
+        for (uint32_t i = 32 + 4 * q4; i < data_c.nw; i += 16) put_seg4(seg, i, load_words4(T, data_c.wa + i));
         // Issue the next slabs' loads, then this slab's A operands.
         SlabData data_n = data_c;
         if (has_n) data_n = slab_data(T, row_e + k0 + kSlabCols, q4, bits_n);
@@ -227,8 +235,8 @@ void afx_gemm_kernel(const GemmBatch batch) {
         }
         wave_sync();
         uint32_t ex1[8], ex2[8];
-        decode_group(seg, (uint32_t)umin64(bit1(bits_c) - 32 * data_c.wa, 32 * (kSegWords - 2)), lut, ex1);
-        decode_group(seg, (uint32_t)umin64(bit2(bits_c) - 32 * data_c.wa, 32 * (kSegWords - 2)), lut, ex2);
+        decode_groups(seg, (uint32_t)umin64(bit1(bits_c) - 32 * data_c.wa, 32 * kSegRev),
+                      (uint32_t)umin64(bit2(bits_c) - 32 * data_c.wa, 32 * kSegRev), lut, ex1, ex2);
         // Join and put both groups into the slab.
         const uint32_t b1[8] = {data_c.s1a.x, data_c.s1a.y, data_c.s1a.z, data_c.s1a.w,
                                 data_c.s1b.x, data_c.s1b.y, data_c.s1b.z, data_c.s1b.w};
@@ -326,8 +334,11 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     if (tiles == 0) return AFX_OK;
     if (tiles >= (1ull << 31)) return AFX_E_UNSUPPORTED;
     const uint32_t tok_blocks = (m + kTileTokens - 1) / kTileTokens;
-    hipLaunchKernelGGL(afx_gemm_kernel, dim3((unsigned)tiles, tok_blocks), dim3(kGemmThreads), 0, stream, batch);
-    return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
+    void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
+    return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemm_kernel), dim3((unsigned)tiles, tok_blocks),
+                           dim3(kGemmThreads), args, 0, stream) == hipSuccess
+               ? AFX_OK
+               : AFX_E_HIP;
 }
 
 }  // namespace

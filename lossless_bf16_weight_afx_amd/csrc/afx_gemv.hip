@@ -290,8 +290,11 @@ int launch_gemv(GemvBatch &batch, hipStream_t stream) {
         batch.j[t].t.blk_lo = (uint32_t)lo;
         batch.j[t].t.blk_hi = (uint32_t)hi;
     }
-    hipLaunchKernelGGL(afx_gemv_kernel<M>, dim3((unsigned)grid), dim3(kThreads), 0, stream, batch);
-    return hipGetLastError() == hipSuccess ? AFX_OK : AFX_E_HIP;
+    void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
+    return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemv_kernel<M>), dim3((unsigned)grid),
+                           dim3(kThreads), args, 0, stream) == hipSuccess
+               ? AFX_OK
+               : AFX_E_HIP;
 }
 
 int check_gemv_job(const afx_gemv_job &j, uint32_t m) {
