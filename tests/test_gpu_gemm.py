@@ -107,6 +107,20 @@ def test_twelve_bit_codes_and_a_starting_y():
     check(blob, rows, cols, x, m, y0)
 
 
+def test_incompressible_exponents():
+    """Uniformly random exponent bytes (8-bit codes, nothing to compress):
+    every row's code words for a 256-column slab are the longest the data can
+    make, 2048 bits plus alignment."""
+    say("[gpu] case gemm uniform exponents")
+    rows, cols, m = 64, 512, 8
+    rng = np.random.default_rng(21)
+    e = rng.integers(1, 255, rows * cols).astype(np.uint16)  # no Inf/NaN
+    w = (rng.integers(0, 2, rows * cols).astype(np.uint16) << 15) | (e << 7) | rng.integers(0, 128, rows * cols).astype(np.uint16)
+    blob = oracle.encode(w, (rows, cols))
+    x = synth.f32_to_bf16_bits((rng.standard_normal((m, cols)) * 1e-30).astype(np.float32))
+    check(blob, rows, cols, x, m)
+
+
 def test_layer_batch_one_launch():
     """The seven matrices of one Qwen3-14B-shaped decoder layer in one batch
     call at m = 16; every product within its bound."""
