@@ -322,3 +322,38 @@ def test_tiers_every_mix_bit_exact(tmp_path):
     p = tiers.plan(st, total // 2, 0, r)
     used = sum(u.bytes if t == "Gc" else (2 * u.n_values if t == "G" else 0) for u, t in zip(st.units, p))
     assert used <= total // 2 and "D" in p
+
+
+def test_graph_replays_bit_exact():
+    """Restores captured into one HIP graph (through torch.cuda.graph) and
+    replayed: the library neither allocates nor clears memory on the stream,
+    so its launches can be captured. Every replay restores into outputs that
+    eager work has overwritten since the last one, and is checked bit for
+    bit."""
+    T = synth.TensorSpec
+    specs = [T("g0", (700, 512), "normal", 901), T("g1", (4096,), "t4", 902), T("g2", (128, 4096), "normal", 903)]
+    xs = [synth.generate(sp) for sp in specs]
+    blobs = [oracle.encode(x, sp.shape) for x, sp in zip(xs, specs)]
+    infos = [afx.afx_query(b) for b in blobs]
+    dblobs = [afx.to_device(b) for b in blobs]
+    outs = [torch.zeros(x.size, dtype=torch.int16, device="cuda") for x in xs]
+    jobs = afx.make_jobs([(i, db.data_ptr(), o.data_ptr(), 2 * x.size) for i, db, o, x in zip(infos, dblobs, outs, xs)])
+    refs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs]
+    say("[gpu] case graph capture of a 3-tensor restore")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        afx.afx_decode_layer_async(jobs, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        afx.afx_decode_layer_async(jobs, torch.cuda.current_stream().cuda_stream)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(0x1234 + rep)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, refs):
+            assert torch.equal(o, r), f"replay {rep}"

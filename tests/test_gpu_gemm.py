@@ -145,3 +145,31 @@ def test_layer_batch_one_launch():
         ref, bound = oracle.restore_gemv(blob, sp.shape[0], sp.shape[1], x, threads=16)
         err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
         assert np.all(err <= 2 * bound), sp.name
+
+
+def test_batches_over_sixteen_matrices():
+    """Eighteen matrices in one batch call of each fused entry point: two
+    launches each (16 + 2); every product within its bound."""
+    rng = np.random.default_rng(77)
+    mats = []
+    for t in range(18):
+        rows, cols = 64 * (1 + t % 3), 256 * (1 + t % 4)
+        w = synth.generate(synth.TensorSpec(f"b{t}", (rows, cols), "normal", 800 + t))
+        blob = oracle.encode(w, (rows, cols))
+        mats.append((blob, rows, cols, afx.afx_query(blob), afx.to_device(blob)))
+    for name, m, call, tol in [("gemv", 4, afx.afx_restore_gemv_batch_async, 1.0),
+                               ("gemm", 5, afx.afx_restore_gemm_batch_async, 2.0)]:
+        say(f"[gpu] case {name} batch of 18 matrices, m={m}")
+        jobs, keep = [], []
+        for blob, rows, cols, info, db in mats:
+            x = synth.f32_to_bf16_bits(rng.standard_normal((m, cols)).astype(np.float32))
+            xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+            y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+            keep.append((x, xd, y))
+            jobs.append((info, db.data_ptr(), rows, cols, xd.data_ptr(), y.data_ptr()))
+        call(jobs, m, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for (blob, rows, cols, _, _), (x, _, y) in zip(mats, keep):
+            ref, bound = oracle.restore_gemv(blob, rows, cols, x)
+            err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+            assert np.all(err <= tol * bound), (name, rows, cols)
