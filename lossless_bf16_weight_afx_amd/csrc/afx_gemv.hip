@@ -13,9 +13,11 @@
 //
 // W is row-major [rows, cols] (the blob's element order), x is BF16 [m, cols]
 // and y is FP32 [m, rows], both row-major; m is 1, 2 or 4 (a handful of
-// tokens). The products of two BF16 values are exact in FP32; sums are FP32,
-// per lane over 8 consecutive values, then across the wave, then into y with
-// atomic adds (in no fixed order).
+// tokens). The products of two BF16 values are exact in FP32; sums are FP32:
+// per lane over 8 consecutive values, two products at a time
+// (v_dot2_f32_bf16, which on this hardware measures within one rounding per
+// addition), then across the wave, then into y with atomic adds (in no fixed
+// order).
 //
 // Work decomposition as in the restore: one 16-wave workgroup per CU, chunks
 // round the workgroups, claimed one at a time by the waves from an LDS
@@ -45,8 +47,8 @@ struct GemvBatch {
     uint32_t n;
 };
 
-__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline bf16x2 bf16_pair(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
 // Sum over the wave with DPP moves (no LDS); the total lands in lane 63.
 template <int kCtrl, int kRowMask = 0xF>
@@ -117,21 +119,17 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t
         if (i + 8 <= ne) {
             const uint2 b = smv[r];
             const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
-            const uint32_t w01 = join_pair<false>(b.x, e.x), w23 = join_pair<true>(b.x, e.x);
-            const uint32_t w45 = join_pair<false>(b.y, e.y), w67 = join_pair<true>(b.y, e.y);
-            const float w[8] = {bf16_lo(w01), bf16_hi(w01), bf16_lo(w23), bf16_hi(w23),
-                                bf16_lo(w45), bf16_hi(w45), bf16_lo(w67), bf16_hi(w67)};
+            // restored values as BF16 pairs (element 2q in the low half),
+            // multiplied two at a time against x's pairs
+            const bf16x2 w01 = bf16_pair(join_pair<false>(b.x, e.x)), w23 = bf16_pair(join_pair<true>(b.x, e.x));
+            const bf16x2 w45 = bf16_pair(join_pair<false>(b.y, e.y)), w67 = bf16_pair(join_pair<true>(b.y, e.y));
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const uint4 xv = *reinterpret_cast<const uint4 *>(x + (uint64_t)m * a.cols + col);
-                float s = w[0] * bf16_lo(xv.x);
-                s = fmaf(w[1], bf16_hi(xv.x), s);
-                s = fmaf(w[2], bf16_lo(xv.y), s);
-                s = fmaf(w[3], bf16_hi(xv.y), s);
-                s = fmaf(w[4], bf16_lo(xv.z), s);
-                s = fmaf(w[5], bf16_hi(xv.z), s);
-                s = fmaf(w[6], bf16_lo(xv.w), s);
-                s = fmaf(w[7], bf16_hi(xv.w), s);
+                float s = __builtin_amdgcn_fdot2_f32_bf16(w01, bf16_pair(xv.x), 0.f, false);
+                s = __builtin_amdgcn_fdot2_f32_bf16(w23, bf16_pair(xv.y), s, false);
+                s = __builtin_amdgcn_fdot2_f32_bf16(w45, bf16_pair(xv.z), s, false);
+                s = __builtin_amdgcn_fdot2_f32_bf16(w67, bf16_pair(xv.w), s, false);
                 acc[r][m] = s;
             }
         } else {
