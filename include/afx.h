@@ -157,7 +157,8 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
  * so their order (and the last bits) may differ between calls. The caller
  * owns y and its initial contents. Enqueued on stream; returns without
  * waiting. Errors: as afx_decode_layer_async; AFX_E_INVALID_ARG (rows *
- * cols != n_elems, NULL pointer), AFX_E_UNSUPPORTED (cols not a multiple of
+ * cols != n_elems, NULL pointer, y sharing a byte with the blob or x),
+ * AFX_E_UNSUPPORTED (cols not a multiple of
  * 8 or above 2^32 - 1; m not 1, 2 or 4), AFX_E_MISALIGNED (blob or x not
  * 16-byte aligned, y not 4-byte aligned). */
 int afx_restore_gemv_async(const afx_info *info, const void *blob_dev, uint64_t rows, uint64_t cols,
@@ -176,8 +177,9 @@ typedef struct afx_gemv_job {
 
 /* afx_restore_gemv_batch_async: afx_restore_gemv_async for every job (all
  * with the same m), one launch per AFX_MAX_GEMV_JOBS_PER_LAUNCH jobs; all
- * jobs are checked before anything is enqueued. Errors as
- * afx_restore_gemv_async. */
+ * jobs are checked before anything is enqueued. Jobs may share x and may
+ * add into the same y; no job's y may share a byte with any job's blob or
+ * x (AFX_E_INVALID_ARG). Errors otherwise as afx_restore_gemv_async. */
 int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream);
 
 /* ---- The restore fused into a product over many tokens (prefill). The
@@ -194,7 +196,8 @@ int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32
  * so their order (and the last bits) may differ between calls. The caller
  * owns y and its initial contents. Enqueued on stream; returns without
  * waiting. Errors: as afx_decode_layer_async; AFX_E_INVALID_ARG (rows *
- * cols != n_elems, a zero size, NULL pointer), AFX_E_UNSUPPORTED (rows not
+ * cols != n_elems, a zero size, NULL pointer, y sharing a byte with the
+ * blob or x), AFX_E_UNSUPPORTED (rows not
  * a multiple of 64, cols not a multiple of 256, either >= 2^31, m == 0 or
  * m > 8388480), AFX_E_MISALIGNED (blob or x not 16-byte aligned, y not
  * 4-byte aligned). */
@@ -203,8 +206,9 @@ int afx_restore_gemm_async(const afx_info *info, const void *blob_dev, uint64_t 
 
 /* afx_restore_gemm_batch_async: afx_restore_gemm_async for every job (all
  * with the same m), one launch per AFX_MAX_GEMV_JOBS_PER_LAUNCH jobs; all
- * jobs are checked before anything is enqueued. Errors as
- * afx_restore_gemm_async. */
+ * jobs are checked before anything is enqueued. Jobs may share x and may
+ * add into the same y; no job's y may share a byte with any job's blob or
+ * x (AFX_E_INVALID_ARG). Errors otherwise as afx_restore_gemm_async. */
 int afx_restore_gemm_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, void *stream);
 
 /* ---- Unpack on the host. "Why Weight Offloading Slows Inference" (section

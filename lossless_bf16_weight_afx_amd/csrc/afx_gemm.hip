@@ -354,6 +354,7 @@ int afx_restore_gemm_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32
         const int rc = check_gemm_job(jobs[i], m);
         if (rc != AFX_OK) return rc;
     }
+    if (fused_outputs_overlap_inputs(jobs, n_jobs, m)) return AFX_E_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (size_t i = 0; i < n_jobs; i += AFX_MAX_GEMV_JOBS_PER_LAUNCH) {
         const size_t k = std::min<size_t>(AFX_MAX_GEMV_JOBS_PER_LAUNCH, n_jobs - i);

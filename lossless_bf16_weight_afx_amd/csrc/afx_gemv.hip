@@ -344,6 +344,7 @@ extern "C" int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_j
         const int rc = check_gemv_job(jobs[i], m);
         if (rc != AFX_OK) return rc;
     }
+    if (fused_outputs_overlap_inputs(jobs, n_jobs, m)) return AFX_E_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (size_t i = 0; i < n_jobs;) {
         GemvBatch batch;

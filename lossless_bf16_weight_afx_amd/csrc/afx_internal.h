@@ -29,4 +29,25 @@ void canonical(const uint8_t len[256], uint32_t code[256]);
 int validate(const uint8_t *blob, size_t nbytes, afx_info *out);
 int check_info(const afx_info *info);
 
+// Whether byte ranges [a, a + an) and [b, b + bn) share a byte.
+inline bool ranges_overlap(const void *a, uint64_t an, const void *b, uint64_t bn) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return an && bn && a0 < b0 + bn && b0 < a0 + an;
+}
+
+// A batch of fused products writes each job's y while it reads every job's
+// blob and x: no y may share a byte with any of them (two jobs may add into
+// the same y, and share x).
+inline bool fused_outputs_overlap_inputs(const afx_gemv_job *jobs, size_t n, uint32_t m) {
+    for (size_t i = 0; i < n; ++i) {
+        const uint64_t ybytes = (uint64_t)m * jobs[i].rows * 4;
+        for (size_t k = 0; k < n; ++k) {
+            if (ranges_overlap(jobs[i].y_dev, ybytes, jobs[k].blob_dev, jobs[k].info->blob_bytes) ||
+                ranges_overlap(jobs[i].y_dev, ybytes, jobs[k].x_dev, (uint64_t)m * jobs[k].cols * 2))
+                return true;
+        }
+    }
+    return false;
+}
+
 }  // namespace afx

@@ -127,3 +127,21 @@ def test_gemm_entry_point_argument_errors():
     assert rc(128, 512, xp=fake + 8) == afx.AFX_E_MISALIGNED
     assert rc(128, 512, y=fake + 2) == afx.AFX_E_MISALIGNED
     assert rc(128, 512, blob=fake + 4) == afx.AFX_E_MISALIGNED
+
+
+def test_fused_outputs_must_not_overlap_inputs():
+    """y sharing a byte with a blob or an x of the batch is refused before
+    any HIP call (fake, never dereferenced addresses)."""
+    afx.lib()
+    x = synth.generate(synth.TensorSpec("t", (128, 512), "normal", 5))
+    info = afx.afx_query(oracle.encode(x, (128, 512)))
+    blob, xp = 1 << 40, 1 << 41
+    for call, m in [(afx.afx_restore_gemv_batch_async, 4), (afx.afx_restore_gemm_batch_async, 8)]:
+        for y in (blob + 256, xp + 64, blob + int(info.blob_bytes) - 4):
+            with pytest.raises(afx.AfxError) as e:
+                call([(info, blob, 128, 512, xp, y)], m, 0)
+            assert e.value.status == afx.AFX_E_INVALID_ARG
+        # another job's blob and x count too
+        with pytest.raises(afx.AfxError) as e:
+            call([(info, blob, 128, 512, xp, 1 << 42), (info, 1 << 43, 128, 512, xp, blob + 16)], m, 0)
+        assert e.value.status == afx.AFX_E_INVALID_ARG
