@@ -111,7 +111,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk", "tiers", "gemv", "gemm"])
+                    choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk", "tiers", "gemv", "gemm",
+                             "token"])
     ap.add_argument("--m", type=int, default=None,
                     help="tokens (activation rows) of the fused products: 1, 2 or 4 for --workload gemv "
                          "(default 1), any for --workload gemm (default 64)")
@@ -149,6 +150,8 @@ def main() -> int:
         return bench_tiers(args, threads)
     if args.workload in ("gemv", "gemm"):
         return bench_gemv(args, threads)
+    if args.workload == "token":
+        return bench_token(args, threads)
     workload, specs = workload_specs(args.workload)
 
     # ---- inputs: generate, encode with the library's encoder, move to HBM
@@ -453,6 +456,139 @@ def bench_gemv(args, threads: int) -> int:
         "config": {"workload": workload, "matrices": len(specs), "weights": n_total, "m": m,
                    "blob_bytes": blob_total, "copies": copies},
         "within_bound": bool(within), "roofline": roofline, "compare": compare, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if within else 1
+
+
+def bench_token(args, threads: int) -> int:
+    """The weights of one generated token, end to end: every matrix of the
+    whole model (40 layers' seven, and the output head) multiplied by the
+    token's activations (m = 1, 2 or 4 rows), straight from the compressed
+    model resident in HBM with the fused matrix-vector kernel, one batch call
+    per unit. Compared with the same products on the BF16 model resident in
+    HBM (torch.mm) and with restoring each unit into one scratch buffer
+    before its products. The embedding lookup reads one row and is left out.
+    The activations are synthetic; nothing between the products (attention,
+    norms) is computed: this times the weight pass the pages' per-token
+    figures are made of."""
+    import torch
+
+    from lossless_bf16_weight_afx_amd import afx, stream, synth
+
+    dev = torch.device("cuda:0")
+    m = args.m if args.m is not None else 1
+    if m not in (1, 2, 4):
+        raise SystemExit("--workload token takes --m 1, 2 or 4")
+    t0 = time.time()
+    units = stream.build_model(synth.model_units(args.layers)[1:], threads=threads, progress=log)  # no embedding
+    log(f"[bench] model store ready in {time.time() - t0:.0f}s")
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    xs = {}  # one activation block per input width, shared by the matrices that read it
+
+    def x_for(cols):
+        if cols not in xs:
+            xs[cols] = torch.randn((m, cols), generator=gen).to(torch.bfloat16).to(dev)
+        return xs[cols]
+
+    blobs, per_unit, unit_mats, mats = [], [], [], []  # mats: (spec, info, device blob address, y)
+    for u in units:
+        db = u.host.to(dev)
+        blobs.append(db)
+        um = []
+        for sp, info, off in zip(u.specs, u.infos, u.offsets):
+            if len(sp.shape) == 2:
+                um.append((sp, info, db.data_ptr() + off, torch.zeros((m, sp.shape[0]), dtype=torch.float32,
+                                                                     device=dev)))
+        per_unit.append(afx.make_gemv_jobs([(info, ptr, sp.shape[0], sp.shape[1], x_for(sp.shape[1]).data_ptr(),
+                                             y.data_ptr()) for sp, info, ptr, y in um]))
+        unit_mats.append(um)
+        mats += um
+    n_weights = sum(int(mt[1].n_elems) for mt in mats)
+    blob_total = sum(int(mt[1].blob_bytes) for mt in mats)
+    stream_ = torch.cuda.current_stream(dev)
+    sp_ = stream_.cuda_stream
+    log(f"[bench] token pass: {len(mats)} matrices, {n_weights} weights, {blob_total} B compressed in HBM")
+
+    def fused(k):
+        for jobs in per_unit:
+            afx.afx_restore_gemv_batch_async(jobs, m, sp_)
+
+    # BF16 copies of every matrix, restored by the library (bit-exact), for
+    # the comparisons and the check
+    wbf = []
+    for sp, info, ptr, _ in mats:
+        w = torch.empty(sp.shape, dtype=torch.bfloat16, device=dev)
+        afx.afx_decode_layer_async(afx.make_jobs([(info, ptr, w.data_ptr(), 2 * int(info.n_elems))]), sp_)
+        wbf.append(w)
+    torch.cuda.synchronize()
+
+    # check (outside the timing): one pass from zero against FP32 products of
+    # the restored weights, within twice the summation bound
+    for _, _, _, y in mats:
+        y.zero_()
+    fused(0)
+    torch.cuda.synchronize()
+    within = True
+    for (sp, _, _, y), w in zip(mats, wbf):
+        wf, xf = w.float(), x_for(sp.shape[1]).float()
+        j = (sp.shape[1] - 1) * 2.0 ** -24
+        bound = j / (1 - j) * (xf.abs() @ wf.abs().t())
+        within &= bool(((y - xf @ wf.t()).abs() <= 2 * bound + 1e-30).all())
+        del wf
+    if not within:
+        log("[bench] fused products fall outside the FP32 summation bound")
+
+    ms_fused = _time_steps(stream_, fused, args.steps, args.warmup)
+
+    def mm(k):
+        for (sp, _, _, _), w in zip(mats, wbf):
+            torch.mm(x_for(sp.shape[1]), w.t())
+
+    ms_mm = _time_steps(stream_, mm, args.steps, args.warmup)
+    del wbf
+    torch.cuda.empty_cache()
+    # restore each unit into one scratch buffer (256-byte aligned outputs),
+    # then multiply
+    slot = lambda n: (n + 127) // 128 * 128
+    scratch = torch.empty(max(sum(slot(int(info.n_elems)) for _, info, _, _ in um) for um in unit_mats),
+                          dtype=torch.bfloat16, device=dev)
+    rjobs, rmats = [], []
+    for um in unit_mats:
+        js, ws, off = [], [], 0
+        for sp, info, ptr, _ in um:
+            n = int(info.n_elems)
+            w = scratch[off:off + n].view(sp.shape)
+            js.append((info, ptr, w.data_ptr(), 2 * n))
+            ws.append((sp, w))
+            off += slot(n)
+        rjobs.append(afx.make_jobs(js))
+        rmats.append(ws)
+
+    def restore_mm(k):
+        for js, ws in zip(rjobs, rmats):
+            afx.afx_decode_layer_async(js, sp_)
+            for sp, w in ws:
+                torch.mm(x_for(sp.shape[1]), w.t())
+
+    ms_rmm = _time_steps(stream_, restore_mm, args.steps, args.warmup)
+    value = 2 * n_weights / (ms_fused * 1e-3) / 1e9
+    line = {
+        "metric": GEMV_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_fused, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 products, f32 sums", "data": "synthetic",
+        "config": {"workload": f"qwen3-14b-model-{args.layers}-layers-token-pass-m{m}", "matrices": len(mats),
+                   "weights": n_weights, "m": m, "blob_bytes": blob_total,
+                   "bf16_bytes": 2 * n_weights, "launches": len(per_unit)},
+        "within_bound": bool(within),
+        "token_pass_ms": {"fused_from_compressed": round(ms_fused, 3), "bf16_resident_torch_mm": round(ms_mm, 3),
+                          "restore_each_unit_then_torch_mm": round(ms_rmm, 3)},
+        "hbm_weight_bytes": {"compressed": blob_total, "bf16": 2 * n_weights},
+        "roofline": {"bound": "hbm", "achieved": round(blob_total / (ms_fused * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(blob_total / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "afx_gemv_kernel"},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
     return 0 if within else 1
