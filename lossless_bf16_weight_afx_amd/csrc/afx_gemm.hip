@@ -168,12 +168,22 @@ __device__ inline SlabData slab_data(const TensorDesc &T, uint64_t e_seg, uint32
     return d;
 }
 
+// The workgroup's LDS as one object, the decode table first: at LDS address
+// 0 a table read needs no base added to its index.
+struct GemmLds {
+    uint16_t lut[kLutEntries];                    // 8 KB
+    uint32_t stage[kTileRows * kSegRow];          // 27 KB
+    uint8_t slab[kTileRows * kSlabStride];        // 33 KB
+    LutScratch scratch;
+};
+
 __global__ __launch_bounds__(kGemmThreads, 2)
 void afx_gemm_kernel(const GemmBatch batch) {
-    __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];                  // 8 KB
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kTileRows * kSegRow];         // 27 KB
-    __shared__ __attribute__((aligned(16))) uint8_t slab[kTileRows * kSlabStride];       // 33 KB
-    __shared__ LutScratch scratch;
+    __shared__ __attribute__((aligned(16))) GemmLds lds;
+    uint16_t *lut = lds.lut;
+    uint32_t *stage = lds.stage;
+    uint8_t *slab = lds.slab;
+    LutScratch &scratch = lds.scratch;
 
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);

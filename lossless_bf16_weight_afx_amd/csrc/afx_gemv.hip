@@ -158,14 +158,26 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t
     }
 }
 
+// The workgroup's LDS as one object, the decode table first: at LDS address
+// 0 a table read needs no base added to its index (the base of a table
+// placed higher does not fit the read instruction's 16-bit offset).
+struct GemvLds {
+    uint16_t lut[kLutEntries];                    // 8 KB
+    uint32_t stage[kWavesPerBlock][kStageRow];    // 98 KB
+    uint16_t xs[kXStageBytes / 2];                // 48 KB
+    LutScratch scratch;
+    uint32_t next_j;  // the workgroup's next unclaimed chunk of the matrix
+};
+
 template <int M>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void afx_gemv_kernel(const GemvBatch batch) {
-    __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];                   // 8 KB
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][kStageRow];  // 98 KB
-    __shared__ LutScratch scratch;
-    __shared__ uint32_t next_j;  // the workgroup's next unclaimed chunk of the matrix
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kXStageBytes / 2];
+    __shared__ __attribute__((aligned(16))) GemvLds lds;
+    uint16_t *lut = lds.lut;
+    auto &stage = lds.stage;
+    LutScratch &scratch = lds.scratch;
+    uint32_t &next_j = lds.next_j;
+    uint16_t *xs = lds.xs;
 
     int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
