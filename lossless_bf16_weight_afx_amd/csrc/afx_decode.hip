@@ -101,10 +101,19 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void afx_decode_kernel(const Batch batch) {
-    __shared__ __attribute__((aligned(16))) uint16_t lut[kLutEntries];  // 8 KB
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kWavesPerBlock][kStageRow];  // 98 KB
-    __shared__ LutScratch scratch;
-    __shared__ uint32_t next_j;  // the workgroup's next unclaimed chunk of the tensor
+    // The workgroup's LDS as one object, the decode table first: at LDS
+    // address 0 a table read needs no base added to its index.
+    struct Lds {
+        uint16_t lut[kLutEntries];                  // 8 KB
+        uint32_t stage[kWavesPerBlock][kStageRow];  // 98 KB
+        LutScratch scratch;
+        uint32_t next_j;  // the workgroup's next unclaimed chunk of the tensor
+    };
+    __shared__ __attribute__((aligned(16))) Lds lds;
+    uint16_t *lut = lds.lut;
+    auto &stage = lds.stage;
+    LutScratch &scratch = lds.scratch;
+    uint32_t &next_j = lds.next_j;
 
     int lane = threadIdx.x & (kWave - 1);
     // the wave index is uniform across the wave: keep it (and everything
