@@ -44,7 +44,7 @@ constexpr uint32_t kTileRows = 64;                           // W rows per tile 
 constexpr uint32_t kSlabCols = 256;                          // columns restored per step
 constexpr uint32_t kRangeSlabs = 10;                         // a tile spans <= 2560 columns
 constexpr uint32_t kRangeCols = kRangeSlabs * kSlabCols;
-constexpr uint32_t kTileTokens = 32 * kGemmWaves;            // 128 tokens per workgroup
+constexpr uint32_t kMaxTokenBlocks = 2;                      // 32-token blocks per wave (1 or 2)
 constexpr uint32_t kRowsPerWave = kTileRows / kGemmWaves;    // 16
 // Code words staged per row segment: 256 codes of <= 12 bits (96 words), the
 // 16-byte alignment of the first word (3), the bit offset inside it and one
@@ -177,6 +177,12 @@ struct GemmLds {
     LutScratch scratch;
 };
 
+// kTB: 32-token blocks per wave, so a workgroup multiplies each restored
+// slab with 128 kTB tokens. With two, only the A operands of the slab's
+// first 4 steps are fetched before the restore; each later step's are
+// fetched 4 steps ahead, during the matrix instructions, to fit the
+// registers.
+template <int kTB>
 __global__ __launch_bounds__(kGemmThreads, 2)
 void afx_gemm_kernel(const GemmBatch batch) {
     __shared__ __attribute__((aligned(16))) GemmLds lds;
@@ -196,7 +202,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t r0 = (tile % J.n_rtiles) * kTileRows;
     const uint32_t kbeg = (tile / J.n_rtiles) * kRangeCols;
     const uint32_t kend = min(J.cols, kbeg + kRangeCols);
-    const uint32_t t0 = blockIdx.y * kTileTokens;
+    const uint32_t t0 = blockIdx.y * (kGemmWaves * 32 * kTB);
     const uint32_t m = batch.m;
 
     build_lut<kGemmThreads>(T.code_len[threadIdx.x], lut, scratch);
@@ -208,11 +214,18 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint64_t row_e = (uint64_t)(r0 + row) * J.cols;              // element of W[r0 + row, 0]
     uint32_t *seg = stage + row * kSegRow;
     uint8_t *out_row = slab + row * kSlabStride;
-    // Multiply: this lane's token (A row) and the wave's token block.
-    const uint32_t tok = t0 + wave * 32 + ((uint32_t)lane & 31);
-    const bool tok_ok = tok < m;
-    const bool wave_mul = t0 + wave * 32 < m;
-    const uint16_t *xa_p = J.x + (uint64_t)(tok_ok ? tok : 0) * J.cols + 8 * ((uint32_t)lane >> 5);
+    // Multiply: this lane's token (A row) in each of the wave's token blocks.
+    const uint32_t t_wave = t0 + wave * 32 * kTB;
+    bool tok_ok[kTB], blk_mul[kTB];
+    const uint16_t *xa_p[kTB];
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
+        const uint32_t tok = t_wave + 32 * tb + ((uint32_t)lane & 31);
+        tok_ok[tb] = tok < m;
+        blk_mul[tb] = t_wave + 32 * tb < m;  // the block holds a token
+        xa_p[tb] = J.x + (uint64_t)(tok_ok[tb] ? tok : 0) * J.cols + 8 * ((uint32_t)lane >> 5);
+    }
+    const bool wave_mul = blk_mul[0];
     const uint8_t *b_row0 = slab + ((uint32_t)lane & 31) * kSlabStride + 16 * ((uint32_t)lane >> 5);
     const uint8_t *b_row1 = b_row0 + 32 * kSlabStride;
 
@@ -225,7 +238,11 @@ void afx_gemm_kernel(const GemmBatch batch) {
     SlabData data_c = slab_data(T, row_e + kbeg, q4, bits_c);
     const bool two = kbeg + kSlabCols < kend;
     SlabBits bits_n = two ? slab_bits(T, row_e + kbeg + kSlabCols, q4) : bits_c;
-    f32x16 acc0 = {}, acc1 = {};
+    f32x16 acc[kTB][2];
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) acc[tb][0] = acc[tb][1] = f32x16{};
+    constexpr uint32_t kSteps = kSlabCols / 16;             // 16-column steps of a slab
+    constexpr uint32_t kPre = kTB == 1 ? kSteps : kSteps / 4;  // A steps fetched before the restore
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
@@ -238,10 +255,12 @@ void afx_gemm_kernel(const GemmBatch batch) {
         if (has_n) data_n = slab_data(T, row_e + k0 + kSlabCols, q4, bits_n);
         SlabBits bits_nn = bits_n;
         if (has_nn) bits_nn = slab_bits(T, row_e + k0 + 2 * kSlabCols, q4);
-        bf16x8 xa[kSlabCols / 16];
+        bf16x8 xa[kSteps][kTB];
         if (wave_mul) {
 #pragma unroll
-            for (uint32_t ks = 0; ks < kSlabCols / 16; ++ks) xa[ks] = load_a(xa_p + k0 + 16 * ks, tok_ok);
+            for (uint32_t ks = 0; ks < kPre; ++ks)
+#pragma unroll
+                for (int tb = 0; tb < kTB; ++tb) xa[ks][tb] = load_a(xa_p[tb] + k0 + 16 * ks, tok_ok[tb]);
         }
         wave_sync();
         uint32_t ex1[8], ex2[8];
@@ -266,11 +285,20 @@ void afx_gemm_kernel(const GemmBatch batch) {
         __syncthreads();  // the slab is complete
         if (wave_mul) {
 #pragma unroll
-            for (uint32_t ks = 0; ks < kSlabCols / 16; ++ks) {
+            for (uint32_t ks = 0; ks < kSteps; ++ks) {
+                if (ks + kPre < kSteps) {
+#pragma unroll
+                    for (int tb = 0; tb < kTB; ++tb)
+                        xa[ks + kPre][tb] = load_a(xa_p[tb] + k0 + 16 * (ks + kPre), tok_ok[tb]);
+                }
                 const bf16x8 w0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row0 + 32 * ks));
                 const bf16x8 w1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row1 + 32 * ks));
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks], w0, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks], w1, acc1, 0, 0, 0);
+#pragma unroll
+                for (int tb = 0; tb < kTB; ++tb) {
+                    if (!blk_mul[tb]) continue;  // uniform: no token of this block is below m
+                    acc[tb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks][tb], w0, acc[tb][0], 0, 0, 0);
+                    acc[tb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks][tb], w1, acc[tb][1], 0, 0, 0);
+                }
             }
         }
         __syncthreads();  // every wave is done with the slab and its staged words
@@ -281,14 +309,16 @@ void afx_gemm_kernel(const GemmBatch batch) {
     if (!wave_mul) return;
     const uint32_t col = r0 + ((uint32_t)lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const uint32_t t = t0 + wave * 32 + 8 * (v / 4) + 4 * ((uint32_t)lane >> 5) + (v & 3);
-        if (t < m) {
-            float *yr = J.y + (uint64_t)t * J.rows;
-            atomicAdd(yr + col, acc0[v]);
-            atomicAdd(yr + col + 32, acc1[v]);
+    for (int tb = 0; tb < kTB; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const uint32_t t = t_wave + 32 * tb + 8 * (v / 4) + 4 * ((uint32_t)lane >> 5) + (v & 3);
+            if (t < m) {
+                float *yr = J.y + (uint64_t)t * J.rows;
+                atomicAdd(yr + col, acc[tb][0][v]);
+                atomicAdd(yr + col + 32, acc[tb][1][v]);
+            }
         }
-    }
 }
 
 }  // namespace
@@ -298,7 +328,7 @@ int check_gemm_job(const afx_gemv_job &j, uint32_t m) {
     if (rc != AFX_OK) return rc;
     if (!j.blob_dev || !j.x_dev || !j.y_dev || j.rows == 0 || j.cols == 0) return AFX_E_INVALID_ARG;
     if (j.rows * j.cols != j.info->n_elems || j.info->n_elems / j.cols != j.rows) return AFX_E_INVALID_ARG;
-    if (m == 0 || m > 65535u * kTileTokens) return AFX_E_UNSUPPORTED;
+    if (m == 0 || m > 65535u * kGemmWaves * 32 * kMaxTokenBlocks) return AFX_E_UNSUPPORTED;
     if (j.rows % kTileRows || j.cols % kSlabCols || j.rows >= (1ull << 31) || j.cols >= (1ull << 31))
         return AFX_E_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(j.blob_dev) & 15) || (reinterpret_cast<uintptr_t>(j.x_dev) & 15) ||
@@ -343,10 +373,14 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     }
     if (tiles == 0) return AFX_OK;
     if (tiles >= (1ull << 31)) return AFX_E_UNSUPPORTED;
-    const uint32_t tok_blocks = (m + kTileTokens - 1) / kTileTokens;
+    // one 32-token block per wave while 128 tokens cover m, else two
+    const uint32_t tb = m <= kGemmWaves * 32 ? 1 : 2;
+    const uint32_t per_wg = kGemmWaves * 32 * tb;
+    const uint32_t tok_blocks = (m + per_wg - 1) / per_wg;
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
-    return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemm_kernel), dim3((unsigned)tiles, tok_blocks),
-                           dim3(kGemmThreads), args, 0, stream) == hipSuccess
+    const void *fn = tb == 1 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1>)
+                             : reinterpret_cast<const void *>(&afx_gemm_kernel<2>);
+    return hipLaunchKernel(fn, dim3((unsigned)tiles, tok_blocks), dim3(kGemmThreads), args, 0, stream) == hipSuccess
                ? AFX_OK
                : AFX_E_HIP;
 }

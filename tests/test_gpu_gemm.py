@@ -53,6 +53,7 @@ def small_ints(rng, shape, lo, hi):
     (128, 768, 37),     # two row tiles, three slabs, a partial token block
     (192, 2816, 130),   # two column ranges (2560 + 256), two token blocks
     (64, 17408, 64),    # down_proj-shaped rows: seven column ranges
+    (128, 512, 300),    # two token blocks per wave, two token tiles, the last one partial
 ])
 def test_integer_data_exact(rows, cols, m):
     say(f"[gpu] case gemm integers {rows}x{cols} m={m}")
