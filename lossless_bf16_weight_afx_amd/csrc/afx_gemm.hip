@@ -181,7 +181,10 @@ struct GemmLds {
 // slab with 128 kTB tokens. With two, only the A operands of the slab's
 // first 4 steps are fetched before the restore; each later step's are
 // fetched 4 steps ahead, during the matrix instructions, to fit the
-// registers.
+// registers. kTB = 0: one block of 32 tokens for the whole workgroup (m <=
+// 32), and the slab's 16 steps split over the waves (4 each), each wave
+// adding its partial sums into y, so that no wave multiplies alone while
+// the others wait.
 template <int kTB>
 __global__ __launch_bounds__(kGemmThreads, 2)
 void afx_gemm_kernel(const GemmBatch batch) {
@@ -202,7 +205,9 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t r0 = (tile % J.n_rtiles) * kTileRows;
     const uint32_t kbeg = (tile / J.n_rtiles) * kRangeCols;
     const uint32_t kend = min(J.cols, kbeg + kRangeCols);
-    const uint32_t t0 = blockIdx.y * (kGemmWaves * 32 * kTB);
+    constexpr bool kSplit = kTB == 0;
+    constexpr int kB = kSplit ? 1 : kTB;  // token blocks per wave
+    const uint32_t t0 = blockIdx.y * (kSplit ? 32 : kGemmWaves * 32 * kTB);
     const uint32_t m = batch.m;
 
     build_lut<kGemmThreads>(T.code_len[threadIdx.x], lut, scratch);
@@ -215,11 +220,11 @@ void afx_gemm_kernel(const GemmBatch batch) {
     uint32_t *seg = stage + row * kSegRow;
     uint8_t *out_row = slab + row * kSlabStride;
     // Multiply: this lane's token (A row) in each of the wave's token blocks.
-    const uint32_t t_wave = t0 + wave * 32 * kTB;
-    bool tok_ok[kTB], blk_mul[kTB];
-    const uint16_t *xa_p[kTB];
+    const uint32_t t_wave = kSplit ? t0 : t0 + wave * 32 * kTB;
+    bool tok_ok[kB], blk_mul[kB];
+    const uint16_t *xa_p[kB];
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
+    for (int tb = 0; tb < kB; ++tb) {
         const uint32_t tok = t_wave + 32 * tb + ((uint32_t)lane & 31);
         tok_ok[tb] = tok < m;
         blk_mul[tb] = t_wave + 32 * tb < m;  // the block holds a token
@@ -238,11 +243,14 @@ void afx_gemm_kernel(const GemmBatch batch) {
     SlabData data_c = slab_data(T, row_e + kbeg, q4, bits_c);
     const bool two = kbeg + kSlabCols < kend;
     SlabBits bits_n = two ? slab_bits(T, row_e + kbeg + kSlabCols, q4) : bits_c;
-    f32x16 acc[kTB][2];
+    f32x16 acc[kB][2];
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) acc[tb][0] = acc[tb][1] = f32x16{};
-    constexpr uint32_t kSteps = kSlabCols / 16;             // 16-column steps of a slab
-    constexpr uint32_t kPre = kTB == 1 ? kSteps : kSteps / 4;  // A steps fetched before the restore
+    for (int tb = 0; tb < kB; ++tb) acc[tb][0] = acc[tb][1] = f32x16{};
+    // 16-column steps of a slab that this wave multiplies: all, or its 4
+    // (steps 4 wave .. 4 wave + 3) when split
+    constexpr uint32_t kSteps = kSplit ? kSlabCols / 16 / kGemmWaves : kSlabCols / 16;
+    const uint32_t ks0 = kSplit ? kSteps * wave : 0;
+    constexpr uint32_t kPre = kTB == 2 ? kSteps / 4 : kSteps;  // A steps fetched before the restore
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
@@ -255,12 +263,12 @@ void afx_gemm_kernel(const GemmBatch batch) {
         if (has_n) data_n = slab_data(T, row_e + k0 + kSlabCols, q4, bits_n);
         SlabBits bits_nn = bits_n;
         if (has_nn) bits_nn = slab_bits(T, row_e + k0 + 2 * kSlabCols, q4);
-        bf16x8 xa[kSteps][kTB];
+        bf16x8 xa[kSteps][kB];
         if (wave_mul) {
 #pragma unroll
             for (uint32_t ks = 0; ks < kPre; ++ks)
 #pragma unroll
-                for (int tb = 0; tb < kTB; ++tb) xa[ks][tb] = load_a(xa_p[tb] + k0 + 16 * ks, tok_ok[tb]);
+                for (int tb = 0; tb < kB; ++tb) xa[ks][tb] = load_a(xa_p[tb] + k0 + 16 * (ks0 + ks), tok_ok[tb]);
         }
         wave_sync();
         uint32_t ex1[8], ex2[8];
@@ -288,13 +296,14 @@ void afx_gemm_kernel(const GemmBatch batch) {
             for (uint32_t ks = 0; ks < kSteps; ++ks) {
                 if (ks + kPre < kSteps) {
 #pragma unroll
-                    for (int tb = 0; tb < kTB; ++tb)
-                        xa[ks + kPre][tb] = load_a(xa_p[tb] + k0 + 16 * (ks + kPre), tok_ok[tb]);
+                    for (int tb = 0; tb < kB; ++tb)
+                        xa[ks + kPre][tb] = load_a(xa_p[tb] + k0 + 16 * (ks0 + ks + kPre), tok_ok[tb]);
                 }
-                const bf16x8 w0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row0 + 32 * ks));
-                const bf16x8 w1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row1 + 32 * ks));
+                const uint32_t kb = 32 * (ks0 + ks);  // the step's byte offset in a slab row
+                const bf16x8 w0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row0 + kb));
+                const bf16x8 w1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(b_row1 + kb));
 #pragma unroll
-                for (int tb = 0; tb < kTB; ++tb) {
+                for (int tb = 0; tb < kB; ++tb) {
                     if (!blk_mul[tb]) continue;  // uniform: no token of this block is below m
                     acc[tb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks][tb], w0, acc[tb][0], 0, 0, 0);
                     acc[tb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks][tb], w1, acc[tb][1], 0, 0, 0);
@@ -309,7 +318,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     if (!wave_mul) return;
     const uint32_t col = r0 + ((uint32_t)lane & 31);
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb)
+    for (int tb = 0; tb < kB; ++tb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const uint32_t t = t_wave + 32 * tb + 8 * (v / 4) + 4 * ((uint32_t)lane >> 5) + (v & 3);
@@ -373,13 +382,15 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     }
     if (tiles == 0) return AFX_OK;
     if (tiles >= (1ull << 31)) return AFX_E_UNSUPPORTED;
-    // one 32-token block per wave while 128 tokens cover m, else two
-    const uint32_t tb = m <= kGemmWaves * 32 ? 1 : 2;
-    const uint32_t per_wg = kGemmWaves * 32 * tb;
+    // one block of 32 tokens shared by the waves while it covers m; one per
+    // wave while 128 cover it; else two per wave
+    const uint32_t tb = m <= 32 ? 0 : m <= kGemmWaves * 32 ? 1 : 2;
+    const uint32_t per_wg = tb == 0 ? 32 : kGemmWaves * 32 * tb;
     const uint32_t tok_blocks = (m + per_wg - 1) / per_wg;
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
-    const void *fn = tb == 1 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1>)
-                             : reinterpret_cast<const void *>(&afx_gemm_kernel<2>);
+    const void *fn = tb == 0   ? reinterpret_cast<const void *>(&afx_gemm_kernel<0>)
+                     : tb == 1 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1>)
+                               : reinterpret_cast<const void *>(&afx_gemm_kernel<2>);
     return hipLaunchKernel(fn, dim3((unsigned)tiles, tok_blocks), dim3(kGemmThreads), args, 0, stream) == hipSuccess
                ? AFX_OK
                : AFX_E_HIP;
