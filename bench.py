@@ -170,8 +170,9 @@ def main() -> int:
         f"(ratio {blob_total / restored:.4f}); inputs ready in {time.time() - t0:.1f}s")
 
     traffic_pass = blob_total + restored
+    # (the timed steps continue the warm-up's rotation, so with more copies
+    # than steps every timed step still finds its copy untouched for ~4 GB)
     copies = args.copies or max(1, int(np.ceil(COLD_BYTES / traffic_pass)))
-    copies = min(copies, max(1, args.steps))  # more would never be touched
     dblobs = [[torch.from_numpy(b).to(dev) for b in blobs] for _ in range(copies)]
     douts = [[torch.empty(int(i.n_elems), dtype=torch.int16, device=dev) for i in infos] for _ in range(copies)]
     jobsets = [afx.make_jobs([(i, b.data_ptr(), o.data_ptr(), 2 * int(i.n_elems))
@@ -207,7 +208,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t_all0.record(stream)
     for k in range(args.steps):
-        afx.afx_decode_layer_async(jobsets[k % copies], sp)
+        afx.afx_decode_layer_async(jobsets[(w + k) % copies], sp)
     t_all1.record(stream)
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
@@ -314,7 +315,7 @@ def _time_steps(stream, fn, steps: int, warmup: int) -> float:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for k in range(steps):
-        fn(k)
+        fn(w + k)  # continuing the warm-up's rotation
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -359,7 +360,6 @@ def bench_gemv(args, threads: int) -> int:
         f"inputs ready in {time.time() - t0:.1f}s")
 
     copies = args.copies or max(1, int(np.ceil(COLD_BYTES / blob_total)))
-    copies = min(copies, max(1, args.steps))
     dblobs = [[torch.from_numpy(b).to(dev) for b in blobs] for _ in range(copies)]
     gen = torch.Generator(device="cpu").manual_seed(7)
     xs = [torch.randn((m, sp.shape[1]), generator=gen).to(torch.bfloat16).to(dev) for sp in specs]
