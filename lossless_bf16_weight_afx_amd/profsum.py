@@ -15,6 +15,10 @@ kernel's sources, so that a reader can tell when the profile is stale.
 
     python -m lossless_bf16_weight_afx_amd.profsum --kernel afx_decode_kernel \\
         --dir D --tag T --bench-args "--workload layer --steps 20 --warmup 3 --no-cpu-baseline"
+
+A second mode, `profsum counters`, keeps the median per dispatch of any
+counters (e.g. SQ instruction and LDS counters, two passes of 8) that
+rocprofv3 --pmc runs recorded for one kernel.
 """
 from __future__ import annotations
 
@@ -119,5 +123,51 @@ achieved_GBps_from_trace = {alg / avg:.1f}
     return 0
 
 
+def counters_main(argv) -> int:
+    """`counters` mode: the median per dispatch of every counter that
+    rocprofv3 --pmc runs recorded for one kernel (several runs, e.g. two
+    passes of 8 SQ counters), written to profiles/<kernel>_<workload>_<name>.txt."""
+    ap = argparse.ArgumentParser(prog="profsum counters")
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--workload", required=True, help="workload name for the file name and header")
+    ap.add_argument("--name", default="sq", help="suffix of the summary's file name")
+    ap.add_argument("--dirs", nargs="+", required=True, help="rocprofv3 -d directories of the runs")
+    ap.add_argument("--commands", nargs="+", required=True, help="the rocprofv3 command of each run")
+    args = ap.parse_args(argv)
+    sys.path.insert(0, ROOT)
+    import bench
+
+    vals = {}
+    for d in args.dirs:
+        found = False
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if not fn.endswith("counter_collection.csv"):
+                    continue
+                found = True
+                per = collections.defaultdict(list)
+                for r in _rows(os.path.join(root, fn)):
+                    if args.kernel in r["Kernel_Name"]:
+                        per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                for k, v in per.items():
+                    vals[k] = statistics.median(v)
+        if not found:
+            raise SystemExit(f"{d}: no counter_collection.csv")
+    lines = [f"# {args.kernel} on {args.workload}: rocprofv3 counters (median per dispatch)",
+             "# (MI355X, gfx950; run from the repository root, TMPDIR=/tmp)", "#"]
+    lines += [f"# run:  {c}" for c in args.commands]
+    lines += [f"# summary: python -m lossless_bf16_weight_afx_amd.profsum counters --kernel {args.kernel} "
+              f"--workload {args.workload} --name {args.name} --dirs ... --commands ...", "#",
+              f"kernel = {args.kernel}", f"kernel_sha = {bench.kernel_sha(args.kernel)}"]
+    lines += [f"{k} = {vals[k]:.6g}" for k in sorted(vals)]
+    txt = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"{args.kernel}_{args.workload}_{args.name}.txt"), "w") as f:
+        f.write(txt)
+    print(txt)
+    return 0
+
+
 if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        raise SystemExit(counters_main(sys.argv[2:]))
     raise SystemExit(main())
