@@ -326,8 +326,8 @@ def bench_gemv(args, threads: int) -> int:
     of one decoder layer, straight from their coded form (one launch per
     step): the matrix-vector kernel (--workload gemv, m = 1, 2 or 4 tokens)
     or the MFMA kernel (--workload gemm, any m). Compared with the same
-    products on the BF16 weights already restored (torch.mm) and with the
-    restore followed by those products."""
+    products on the BF16 weights already restored (torch.mm, and torch.mv
+    at m = 1) and with the restore followed by those products."""
     import torch
 
     from lossless_bf16_weight_afx_amd import afx, synth
@@ -411,8 +411,13 @@ def bench_gemv(args, threads: int) -> int:
         afx.afx_decode_layer_async(djobs[k % copies], sp_)
         mm(k)
 
+    def mv(k):  # torch's matrix-vector path, for one token
+        for x, w in zip(xs, wbf[k % copies]):
+            torch.mv(w, x[0])
+
     ms_mm = _time_steps(stream, mm, args.steps, args.warmup)
     ms_rmm = _time_steps(stream, restore_mm, args.steps, args.warmup)
+    ms_mv = _time_steps(stream, mv, args.steps, args.warmup) if m == 1 else None
     del wbf, djobs
     copy_gbps, copy_each_way = copy_ceiling(stream, 2 * blob_total, copies)  # read and write a layer's blobs
 
@@ -426,6 +431,8 @@ def bench_gemv(args, threads: int) -> int:
     compare = {"unit": "us per layer", "fused": round(ms_fused * 1e3, 1), "fused_hot_one_copy": round(hot_ms * 1e3, 1),
                "bf16_torch_mm_on_restored": round(ms_mm * 1e3, 1),
                "restore_then_bf16_torch_mm": round(ms_rmm * 1e3, 1)}
+    if ms_mv is not None:
+        compare["bf16_torch_mv_on_restored"] = round(ms_mv * 1e3, 1)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -159,7 +159,7 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
  * waiting. Errors: as afx_decode_layer_async; AFX_E_INVALID_ARG (rows *
  * cols != n_elems, NULL pointer, y sharing a byte with the blob or x),
  * AFX_E_UNSUPPORTED (cols not a multiple of
- * 8 or above 2^32 - 1; m not 1, 2 or 4), AFX_E_MISALIGNED (blob or x not
+ * 8 or 2^31 or more; m not 1, 2 or 4), AFX_E_MISALIGNED (blob or x not
  * 16-byte aligned, y not 4-byte aligned). */
 int afx_restore_gemv_async(const afx_info *info, const void *blob_dev, uint64_t rows, uint64_t cols,
                            const uint16_t *x_dev, uint32_t m, float *y_dev, void *stream);

@@ -84,10 +84,8 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
             const uint2 b = smv[r];
             const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
             uint4 o;
-            o.x = join_pair<false>(b.x, e.x);
-            o.y = join_pair<true>(b.x, e.x);
-            o.z = join_pair<false>(b.y, e.y);
-            o.w = join_pair<true>(b.y, e.y);
+            join4(b.x, e.x, o.x, o.y);
+            join4(b.y, e.y, o.z, o.w);
             store_out(out + i, o);
             __builtin_amdgcn_sched_barrier(0);  // keep live ranges per step
         } else {

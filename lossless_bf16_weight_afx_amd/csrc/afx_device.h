@@ -155,19 +155,18 @@ __device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
     }
 }
 
-// Two BF16 values from the sign/mantissa bytes b and exponent bytes e of
-// elements 0,1 (kHigh: of elements 2,3). With v = [e1 b1 e0 b0], each 16-bit
-// half of v is (e << 8) | (s << 7) | m; the result half is
-// (s << 15) | (e << 7) | m.
-template <bool kHigh>
-__device__ inline uint32_t join_pair(uint32_t b, uint32_t e) {
-    // b2, e2: the two elements' bytes in 16-bit lanes. The result half is
-    // (e << 7) + m + (s << 15) = (e << 7) + b + 255 * (b & 0x80), and no
-    // half overflows into the next.
-    constexpr uint32_t sel = kHigh ? 0x0c030c02u : 0x0c010c00u;
-    const uint32_t b2 = __builtin_amdgcn_perm(0u, b, sel);
-    const uint32_t e2 = __builtin_amdgcn_perm(0u, e, sel);
-    return (e2 << 7) + (__umul24(b2 & 0x00800080u, 255u) + b2);
+// Four BF16 values from the sign/mantissa bytes b and exponent bytes e of
+// four consecutive elements (byte k of each word: element k). BF16 is
+// s | e | m (1, 8 and 7 bits): its high byte is (s << 7) | (e >> 1) and its
+// low byte ((e & 1) << 7) | m. One bitfield select forms the four high
+// bytes, one the four low bytes (bits shifted across a byte boundary land
+// only where the mask takes the other operand), and two byte permutes
+// interleave them: w01 holds elements 0 (low half) and 1, w23 elements 2, 3.
+__device__ inline void join4(uint32_t b, uint32_t e, uint32_t &w01, uint32_t &w23) {
+    const uint32_t hi = (b & 0x80808080u) | ((e >> 1) & 0x7F7F7F7Fu);
+    const uint32_t lo = ((e << 7) & 0x80808080u) | (b & 0x7F7F7F7Fu);
+    w01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    w23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
 // Symbols (byte 1 of two table entries) packed as bytes 0,1 of a word.

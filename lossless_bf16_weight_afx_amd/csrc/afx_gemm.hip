@@ -283,12 +283,13 @@ void afx_gemm_kernel(const GemmBatch batch) {
         uint4 *o2 = reinterpret_cast<uint4 *>(out_row + 64 * (q4 + 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            o1[j] = make_uint4(join_pair<false>(b1[2 * j], ex1[2 * j]), join_pair<true>(b1[2 * j], ex1[2 * j]),
-                               join_pair<false>(b1[2 * j + 1], ex1[2 * j + 1]),
-                               join_pair<true>(b1[2 * j + 1], ex1[2 * j + 1]));
-            o2[j] = make_uint4(join_pair<false>(b2[2 * j], ex2[2 * j]), join_pair<true>(b2[2 * j], ex2[2 * j]),
-                               join_pair<false>(b2[2 * j + 1], ex2[2 * j + 1]),
-                               join_pair<true>(b2[2 * j + 1], ex2[2 * j + 1]));
+            uint4 v1, v2;
+            join4(b1[2 * j], ex1[2 * j], v1.x, v1.y);
+            join4(b1[2 * j + 1], ex1[2 * j + 1], v1.z, v1.w);
+            join4(b2[2 * j], ex2[2 * j], v2.x, v2.y);
+            join4(b2[2 * j + 1], ex2[2 * j + 1], v2.z, v2.w);
+            o1[j] = v1;
+            o2[j] = v2;
         }
         __syncthreads();  // the slab is complete
         if (wave_mul) {

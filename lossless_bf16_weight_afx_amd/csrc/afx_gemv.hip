@@ -36,7 +36,7 @@ struct GemvArgs {
     const uint16_t *x;  // [m, cols] BF16
     float *y;           // [m, rows] FP32, accumulated into
     uint64_t rows;
-    uint32_t cols;      // a multiple of 8: every 8 consecutive values lie in one row
+    uint32_t cols;      // a multiple of 8 (every 8 consecutive values lie in one row), below 2^31
     uint32_t reserved;
 };
 
@@ -48,6 +48,10 @@ struct GemvBatch {
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Word 3 of a raw buffer resource on this architecture: 32-bit data format,
+// byte offsets, range-checked against the record count.
+constexpr int kBufferFlags = 0x00020000;
 __device__ inline bf16x2 bf16_pair(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
 // Sum over the wave with DPP moves (no LDS); the total lands in lane 63.
@@ -88,7 +92,7 @@ __device__ inline void load_signmant(const TensorDesc &T, uint64_t lc, int lane,
 // have been used, the bytes of chunk next_lc (if any) are requested into it,
 // so that their latency overlaps the rest of this chunk and the next decode.
 template <int M>
-__device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t lc, uint2 (&smv)[8],
+__device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_in_lds, uint64_t lc, uint2 (&smv)[8],
                                   bool has_next, uint64_t next_lc, const ChunkGeom &g, const Gaps &gaps,
                                   const uint16_t *lut, uint32_t *stage, int lane, uint64_t later_bases,
                                   ChunkGeom &later) {
@@ -105,6 +109,11 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t
     const uint64_t row0 = e0 / a.cols;
     const uint32_t c0 = (uint32_t)(e0 - row0 * a.cols);
     const uint8_t *exb = reinterpret_cast<const uint8_t *>(stage);
+    __amdgpu_buffer_rsrc_t xrow[M];  // row m of x (cols * 2 < 2^32 bytes)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        xrow[m] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.x + (uint64_t)m * a.cols), (short)0,
+                                                    (int)(2 * a.cols), kBufferFlags);
     float acc[8][M];
     uint32_t drow[8];
 #pragma unroll
@@ -121,11 +130,23 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t
             const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
             // restored values as BF16 pairs (element 2q in the low half),
             // multiplied two at a time against x's pairs
-            const bf16x2 w01 = bf16_pair(join_pair<false>(b.x, e.x)), w23 = bf16_pair(join_pair<true>(b.x, e.x));
-            const bf16x2 w45 = bf16_pair(join_pair<false>(b.y, e.y)), w67 = bf16_pair(join_pair<true>(b.y, e.y));
+            uint32_t p01, p23, p45, p67;
+            join4(b.x, e.x, p01, p23);
+            join4(b.y, e.y, p45, p67);
+            const bf16x2 w01 = bf16_pair(p01), w23 = bf16_pair(p23), w45 = bf16_pair(p45), w67 = bf16_pair(p67);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const uint4 xv = *reinterpret_cast<const uint4 *>(x + (uint64_t)m * a.cols + col);
+                // The staged copy is read with an LDS load and x in L2 with
+                // a buffer load: as two plain loads, the compiler merges
+                // them into one generic (flat) load of a selected pointer,
+                // which waits on both memory counters.
+                uint4 xv;
+                if (x_in_lds) {
+                    xv = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * a.cols + col);
+                } else {
+                    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xrow[m], 2 * col, 0, 0);
+                    xv = make_uint4(t.x, t.y, t.z, t.w);
+                }
                 float s = __builtin_amdgcn_fdot2_f32_bf16(w01, bf16_pair(xv.x), 0.f, false);
                 s = __builtin_amdgcn_fdot2_f32_bf16(w23, bf16_pair(xv.y), s, false);
                 s = __builtin_amdgcn_fdot2_f32_bf16(w45, bf16_pair(xv.z), s, false);
@@ -138,7 +159,7 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *x, uint64_t
                 const float w = __uint_as_float((((bb & 0x80u) << 8) | (ee << 7) | (bb & 0x7Fu)) << 16);
 #pragma unroll
                 for (int m = 0; m < M; ++m)
-                    acc[r][m] = fmaf(w, __uint_as_float((uint32_t)x[(uint64_t)m * a.cols + col + (j - i)] << 16),
+                    acc[r][m] = fmaf(w, __uint_as_float((uint32_t)a.x[(uint64_t)m * a.cols + col + (j - i)] << 16),
                                      acc[r][m]);
             }
         }
@@ -219,7 +240,6 @@ void afx_gemv_kernel(const GemvBatch batch) {
         build_lut(len, lut, scratch);  // ends with a barrier
         __syncthreads();
         if (!has_c) continue;
-        const uint16_t *x = x_in_lds ? xs : a.x;
         uint2 smv[8];
         load_signmant(T, k + (uint64_t)jc * nb, lane, smv);
         put_stream(T, g, s, my_stage, lane);
@@ -242,7 +262,7 @@ void afx_gemv_kernel(const GemvBatch batch) {
                 if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
             }
             ChunkGeom gnn;
-            gemv_chunk<M>(a, x, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, lut, my_stage,
+            gemv_chunk<M>(a, xs, x_in_lds, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, lut, my_stage,
                           lane, bases_nn, gnn);
             if (!has_n) break;
             wave_sync();  // the exponent bytes have been read
@@ -314,7 +334,7 @@ int check_gemv_job(const afx_gemv_job &j, uint32_t m) {
     if (j.cols == 0 || info->n_elems % j.cols || info->n_elems / j.cols != j.rows) return AFX_E_INVALID_ARG;
     if (info->n_elems == 0) return AFX_OK;  // nothing to add
     if (!j.blob_dev) return AFX_E_INVALID_ARG;
-    if (j.cols % 8 || j.cols > 0xFFFFFFFFull) return AFX_E_UNSUPPORTED;
+    if (j.cols % 8 || j.cols >= (1ull << 31)) return AFX_E_UNSUPPORTED;  // x rows are read by byte offset
     if (m != 1 && m != 2 && m != 4) return AFX_E_UNSUPPORTED;
     if (!j.x_dev || !j.y_dev) return AFX_E_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(j.blob_dev) | reinterpret_cast<uintptr_t>(j.x_dev)) & 15) return AFX_E_MISALIGNED;
