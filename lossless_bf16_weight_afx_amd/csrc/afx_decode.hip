@@ -125,13 +125,13 @@ void afx_decode_kernel(const Batch batch) {
         // Workgroups [blk_lo, blk_hi) serve T (the host splits the grid among
         // the tensors in proportion to their chunk counts). Within a tensor the
         // chunks go round its workgroups, so that all of them move through each
-        // array together, in one narrow band: the k-th of nb takes chunks
-        // k + j nb, j = 0, 1, ... Wave w starts with j = w and j = w + 16;
+        // array together, in one narrow band: the workgroup of rank k of nb
+        // (ranks counted XCD by XCD) takes chunks k + j nb, j = 0, 1, ... Wave w starts with j = w and j = w + 16;
         // after that each wave claims the next unclaimed j when it starts a
         // chunk, so waves that the SIMDs serve faster restore more chunks and
         // all finish together.
         if (b < T.blk_lo || b >= T.blk_hi) continue;
-        const uint32_t k = (uint32_t)b - T.blk_lo, nb = T.blk_hi - T.blk_lo;
+        const uint32_t nb = T.blk_hi - T.blk_lo, k = xcd_rank((uint32_t)b - T.blk_lo, nb);
         if (k >= T.n_chunks) continue;
         const uint32_t mine = (T.n_chunks - k + nb - 1) / nb;
         uint32_t jc = wave, jn = wave + kWavesPerBlock;

@@ -59,6 +59,18 @@ static_assert(kRev % 4 == 3, "reversed staging needs kRev = 3 mod 4");
 // slice starts 16-byte aligned.
 constexpr uint32_t kStageRow = (kStageWords + 1 + 3) & ~3u;
 
+// Rank of the k-th of nb workgroups that serve one tensor, counted XCD by
+// XCD. The grid's workgroups go to the 8 XCDs in turn (workgroup b to XCD
+// b mod 8) and each XCD has its own L2. Chunk c goes to rank c mod nb, so
+// that neighbouring chunks, which share the cache lines at the ends of their
+// code words, are mostly restored on one XCD and those lines are fetched
+// once. A permutation of 0..nb-1.
+__device__ inline uint32_t xcd_rank(uint32_t k, uint32_t nb) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t x = k % kXcds, i = k / kXcds;
+    return x * (nb / kXcds) + min(x, nb % kXcds) + i;
+}
+
 // Order LDS traffic between lanes of one wave (no workgroup barrier needed).
 __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

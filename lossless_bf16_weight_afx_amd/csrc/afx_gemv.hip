@@ -207,11 +207,11 @@ void afx_gemv_kernel(const GemvBatch batch) {
     for (uint32_t t = 0; t < batch.n; ++t) {
         const GemvArgs &a = batch.j[t];
         const TensorDesc &T = a.t;
-        // Workgroups [blk_lo, blk_hi) serve this matrix; the k-th of nb takes
-        // chunks k + j nb; wave w starts with j = w and j = w + 16, then
+        // Workgroups [blk_lo, blk_hi) serve this matrix; the one of rank k of
+        // nb (ranks counted XCD by XCD) takes chunks k + j nb; wave w starts with j = w and j = w + 16, then
         // claims the next unclaimed j.
         if (b < T.blk_lo || b >= T.blk_hi) continue;
-        const uint32_t k = b - T.blk_lo, nb = T.blk_hi - T.blk_lo;
+        const uint32_t nb = T.blk_hi - T.blk_lo, k = xcd_rank(b - T.blk_lo, nb);
         if (k >= T.n_chunks) continue;
         const uint32_t mine = (T.n_chunks - k + nb - 1) / nb;
         uint32_t jc = wave, jn = wave + kWavesPerBlock;
