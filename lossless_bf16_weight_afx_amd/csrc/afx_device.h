@@ -216,12 +216,25 @@ __device__ inline uint32_t chain_pair(Chain &c, const uint32_t *stage, const uin
 // costs two dependent table reads instead of three LDS round trips. Chains A
 // and B advance together so that their reads overlap.
 struct BufChain {
-    uint32_t r, hi, lo, nx;
+    uint32_t r, q, hi, lo, nx;  // q = r / 32: hi, lo, nx are staged words q + 1, q, q - 1
 };
 
 __device__ inline BufChain buf_chain(const uint32_t *stage, uint32_t r) {
     const uint32_t *p = stage + (r >> 5);
-    return BufChain{r, p[1], p[0], p[-1]};
+    return BufChain{r, r >> 5, p[1], p[0], p[-1]};
+}
+
+// Consume d bits (at most 24, so the window moves by at most one word).
+// The word index itself tells whether the window moved, and addresses the
+// word read ahead.
+__device__ inline void buf_advance(BufChain &c, const uint32_t *stage, uint32_t d) {
+    c.r -= d;
+    const uint32_t q = c.r >> 5;
+    const bool moved = q != c.q;
+    c.q = q;
+    c.hi = moved ? c.lo : c.hi;
+    c.lo = moved ? c.nx : c.lo;
+    c.nx = stage[q - 1];
 }
 
 __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t *stage, const uint16_t *lut,
@@ -230,18 +243,72 @@ __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t 
     const uint32_t wb = __builtin_amdgcn_alignbit(b.hi, b.lo, b.r);
     const uint32_t a1 = lookup(lut, wa), b1 = lookup(lut, wb);
     const uint32_t a2 = lookup(lut, wa << (a1 & 31)), b2 = lookup(lut, wb << (b1 & 31));
-    const uint32_t da = (a1 + a2) & 0xFF, db = (b1 + b2) & 0xFF;
-    const bool ca = (a.r & 31) < da, cb = (b.r & 31) < db;  // the window moved to the next word
-    a.r -= da;
-    b.r -= db;
-    a.hi = ca ? a.lo : a.hi;
-    b.hi = cb ? b.lo : b.hi;
-    a.lo = ca ? a.nx : a.lo;
-    b.lo = cb ? b.nx : b.lo;
-    a.nx = stage[(a.r >> 5) - 1];
-    b.nx = stage[(b.r >> 5) - 1];
+    buf_advance(a, stage, (a1 + a2) & 0xFF);
+    buf_advance(b, stage, (b1 + b2) & 0xFF);
     sa = sym_pair(a1, a2);
     sb = sym_pair(b1, b2);
+}
+
+// A second table over the same 12-bit windows, for kernels whose decode
+// is bound by instruction issue and LDS rather than by HBM. Entry i
+// (32 bits) describes the codes that start window i:
+//   byte 0   bits to consume: both codes' lengths when the second code also
+//            ends inside the window, else the first code's length;
+//   byte 1   the first code's symbol;
+//   byte 2   the second code's symbol (when both fit, else 0);
+//   byte 3   bits 0-3: the first code's length; bit 7: both codes fit.
+// With mean code lengths near 2.6 bits, two codes fit in 12 bits for about
+// 99.6% of windows, so most two-symbol steps take one table read instead of
+// two dependent ones.
+constexpr uint32_t kPairBit = 0x80000000u;
+
+// Fill the pair table from the one-code table (both in LDS); all kNThreads
+// threads take part, and callers bracket it with barriers.
+template <int kNThreads = kThreads>
+__device__ void build_pair_lut(const uint16_t *lut, uint32_t *plut) {
+    constexpr uint32_t kPer = kLutEntries / kNThreads;
+    static_assert(kLutEntries % kNThreads == 0, "whole entries per thread");
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        const uint32_t i = (uint32_t)threadIdx.x * kPer + k;
+        const uint32_t e1 = lut[i], l1 = e1 & 0xFF;
+        const uint32_t e2 = lut[(i << l1) & (kLutEntries - 1)], l2 = e2 & 0xFF;
+        const bool both = l1 + l2 <= kMaxLen;
+        plut[i] = (both ? l1 + l2 : l1) | (e1 & 0xFF00u) | (both ? (e2 & 0xFF00u) << 8 : 0u) | (l1 << 24) |
+                  (both ? kPairBit : 0u);
+    }
+}
+
+// A pair entry whose window holds only one whole code, completed by the
+// entry e2 of the window shifted past that code.
+__device__ inline uint32_t complete_entry(uint32_t e, uint32_t e2) {
+    return (e & 0xFF00u) | ((e2 & 0xFF00u) << 8) | ((e & 0xFFu) + ((e2 >> 24) & 0xFu));
+}
+
+// The buffered chains (BufChain) advanced through the pair table. Both
+// chains' table reads are issued before the (rare) branch that completes
+// entries holding one code, so that their latencies overlap. ea, eb: the
+// entries (byte 0: bits consumed; bytes 1, 2: the two symbols).
+__device__ inline void pair_chain_steps(BufChain &a, BufChain &b, const uint32_t *stage, const uint32_t *plut,
+                                        uint32_t &ea, uint32_t &eb) {
+    const uint32_t wa = __builtin_amdgcn_alignbit(a.hi, a.lo, a.r);
+    const uint32_t wb = __builtin_amdgcn_alignbit(b.hi, b.lo, b.r);
+    ea = plut[wa >> (32 - kMaxLen)];
+    eb = plut[wb >> (32 - kMaxLen)];
+    if ((int32_t)(ea & eb) >= 0) {  // some entry holds one code: read the second
+        const uint32_t fa = plut[(wa << (ea & 31)) >> (32 - kMaxLen)];
+        const uint32_t fb = plut[(wb << (eb & 31)) >> (32 - kMaxLen)];
+        ea = (int32_t)ea >= 0 ? complete_entry(ea, fa) : ea;
+        eb = (int32_t)eb >= 0 ? complete_entry(eb, fb) : eb;
+    }
+    buf_advance(a, stage, ea & 0xFF);
+    buf_advance(b, stage, eb & 0xFF);
+}
+
+// The symbols (bytes 1, 2) of two pair entries, first then second, as the
+// four bytes of a word.
+__device__ inline uint32_t join_entries(uint32_t first, uint32_t second) {
+    return __builtin_amdgcn_perm(second, first, 0x06050201u);
 }
 
 __device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -377,6 +444,33 @@ __device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, co
             wa[q] = join_halves(a01, a23);
             wb[q] = join_halves(b01, b23);
         }
+    }
+    wave_sync();  // every lane is done reading the staged words
+    uint4 *pa = reinterpret_cast<uint4 *>(stage + lane * 8);
+    uint4 *pb = reinterpret_cast<uint4 *>(stage + (lane + kWave) * 8);
+    pa[0] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    pa[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
+    pb[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    pb[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
+    wave_sync();
+}
+
+// decode_exponents with the buffered chains advanced through the pair
+// table (same clamping, same result).
+__device__ inline void decode_exponents_paired(const ChunkGeom &g, const Gaps &gaps, const uint32_t *plut,
+                                               uint32_t *stage, int lane) {
+    constexpr uint32_t kMaxStart = 32 * (kRev - 13);
+    const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart);
+    const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart);
+    uint32_t wa[8], wb[8];
+    BufChain A = buf_chain(stage, ra), B = buf_chain(stage, rb);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        uint32_t a01, b01, a23, b23;
+        pair_chain_steps(A, B, stage, plut, a01, b01);
+        pair_chain_steps(A, B, stage, plut, a23, b23);
+        wa[q] = join_entries(a01, a23);
+        wb[q] = join_entries(b01, b23);
     }
     wave_sync();  // every lane is done reading the staged words
     uint4 *pa = reinterpret_cast<uint4 *>(stage + lane * 8);

@@ -70,7 +70,7 @@ __device__ inline float wave_sum_to_lane63(float v) {
 }
 
 // Activations of one matrix staged in LDS when they fit (m * cols BF16).
-constexpr uint32_t kXStageBytes = 48 * 1024;
+constexpr uint32_t kXStageBytes = 40 * 1024;  // 4 tokens of 5120 values, one of 17408
 
 // Request chunk lc's sign/mantissa bytes in store order (lane: bytes
 // [r*512 + 8*lane, +8) for r = 0..7); read once, not kept in the caches.
@@ -94,13 +94,13 @@ __device__ inline void load_signmant(const TensorDesc &T, uint64_t lc, int lane,
 template <int M>
 __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_in_lds, uint64_t lc, uint2 (&smv)[8],
                                   bool has_next, uint64_t next_lc, const ChunkGeom &g, const Gaps &gaps,
-                                  const uint16_t *lut, uint32_t *stage, int lane, uint64_t later_bases,
+                                  const uint32_t *plut, uint32_t *stage, int lane, uint64_t later_bases,
                                   ChunkGeom &later) {
     const TensorDesc &T = a.t;
     const uint64_t e0 = lc * kChunk;
     const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
     const uint8_t *sm = T.signmant + e0;
-    decode_exponents<true>(g, gaps, lut, stage, lane);
+    decode_exponents_paired(g, gaps, plut, stage, lane);
     asm volatile("" : "+v"(later_bases));  // not before the decode above
     later = geom_from_lanes(later_bases);
 
@@ -181,11 +181,13 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
 
 // The workgroup's LDS as one object, the decode table first: at LDS address
 // 0 a table read needs no base added to its index (the base of a table
-// placed higher does not fit the read instruction's 16-bit offset).
+// placed higher does not fit the read instruction's 16-bit offset). The
+// one-code table is built in the staging area and turned into the pair
+// table before any chunk is staged.
 struct GemvLds {
-    uint16_t lut[kLutEntries];                    // 8 KB
+    uint32_t plut[kLutEntries];                   // 16 KB
     uint32_t stage[kWavesPerBlock][kStageRow];    // 98 KB
-    uint16_t xs[kXStageBytes / 2];                // 48 KB
+    uint16_t xs[kXStageBytes / 2];                // 40 KB
     LutScratch scratch;
     uint32_t next_j;  // the workgroup's next unclaimed chunk of the matrix
 };
@@ -194,8 +196,10 @@ template <int M>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void afx_gemv_kernel(const GemvBatch batch) {
     __shared__ __attribute__((aligned(16))) GemvLds lds;
-    uint16_t *lut = lds.lut;
+    uint32_t *plut = lds.plut;
     auto &stage = lds.stage;
+    uint16_t *lut = reinterpret_cast<uint16_t *>(&lds.stage[0][0]);  // the one-code table, while building
+    static_assert(sizeof(lds.stage) >= kLutEntries * sizeof(uint16_t), "room for the one-code table");
     LutScratch &scratch = lds.scratch;
     uint32_t &next_j = lds.next_j;
     uint16_t *xs = lds.xs;
@@ -237,8 +241,10 @@ void afx_gemv_kernel(const GemvBatch batch) {
         if (x_in_lds)
             for (uint32_t i = threadIdx.x; i < xbytes / 16; i += kThreads)
                 reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(a.x)[i];
-        build_lut(len, lut, scratch);  // ends with a barrier
+        build_lut(len, lut, scratch);
         __syncthreads();
+        build_pair_lut(lut, plut);
+        __syncthreads();  // the pair table is complete and the staging area free
         if (!has_c) continue;
         uint2 smv[8];
         load_signmant(T, k + (uint64_t)jc * nb, lane, smv);
@@ -262,7 +268,7 @@ void afx_gemv_kernel(const GemvBatch batch) {
                 if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
             }
             ChunkGeom gnn;
-            gemv_chunk<M>(a, xs, x_in_lds, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, lut, my_stage,
+            gemv_chunk<M>(a, xs, x_in_lds, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, plut, my_stage,
                           lane, bases_nn, gnn);
             if (!has_n) break;
             wave_sync();  // the exponent bytes have been read

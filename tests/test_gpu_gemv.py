@@ -51,8 +51,8 @@ def run(w_bits, rows, cols, m, seed, y0=None, dist="normal"):
     (640, 5120, 2),
     (640, 5120, 4),
     (96, 17408, 4),     # down_proj-shaped rows
-    (40, 12288, 2),     # x fills the 48 KB activation stage exactly
-    (50, 12296, 2),     # x 16 bytes over the stage: read from L2
+    (40, 10240, 2),     # x fills the 40 KB activation stage exactly
+    (50, 10248, 2),     # x 16 bytes over the stage: read from L2
     (333, 1000, 2),     # several rows per chunk, short last chunk
     (129, 32, 1),       # 128 rows in a chunk
     (7, 8, 4),          # one tiny chunk
