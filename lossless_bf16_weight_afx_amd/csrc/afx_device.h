@@ -212,9 +212,9 @@ __device__ inline uint32_t chain_pair(Chain &c, const uint32_t *stage, const uin
 }
 
 // The same chain with the two staged words of its window and the word after
-// them kept in registers: the next word is read one pair ahead, so a pair
-// costs two dependent table reads instead of three LDS round trips. Chains A
-// and B advance together so that their reads overlap.
+// them kept in registers: the next word is read one step ahead, so forming a
+// window never waits for LDS. Two such chains advance together (see
+// pair_chain_steps) so that their table reads overlap.
 struct BufChain {
     uint32_t r, q, hi, lo, nx;  // q = r / 32: hi, lo, nx are staged words q + 1, q, q - 1
 };
@@ -237,6 +237,10 @@ __device__ inline void buf_advance(BufChain &c, const uint32_t *stage, uint32_t 
     c.nx = stage[q - 1];
 }
 
+// Two symbols per chain through the one-code table, two dependent table
+// reads per step; sa, sb: the symbols as bytes 0, 1. (The MFMA product,
+// which builds its table once per 64-row tile, measured 7-8% slower with the
+// pair table below.)
 __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t *stage, const uint16_t *lut,
                                        uint32_t &sa, uint32_t &sb) {
     const uint32_t wa = __builtin_amdgcn_alignbit(a.hi, a.lo, a.r);
@@ -410,40 +414,25 @@ __device__ inline void store_out(uint16_t *p, uint4 v) {
 // Decode a staged chunk's 4096 exponent codes and leave the exponent bytes
 // in element order at the start of `stage` (which held the code words).
 // Chain starts are clamped so that 32 decodes (at most 384 bits) never leave
-// the staged words even on a corrupt gap; the buffered chains' read ahead
-// (one word past the window) stays at index >= 0 for the same reason.
-// kBuffered picks the buffered chains (the choice of a kernel whose chunk
-// time the decode latency bounds; the restore, bound by HBM, does not need
-// them).
-template <bool kBuffered = false>
+// the staged words even on a corrupt gap. Plain chains: the choice of a
+// kernel bound by HBM; decode_exponents_paired below is the one for kernels
+// whose chunk time the decode bounds.
 __device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, const uint16_t *lut, uint32_t *stage,
                                         int lane) {
     constexpr uint32_t kMaxStart = 32 * (kRev - 13);
     const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart);
     const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart);
     uint32_t wa[8], wb[8];
-    if (kBuffered) {
-        BufChain A = buf_chain(stage, ra), B = buf_chain(stage, rb);
+    Chain A{ra};
+    Chain B{rb};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            uint32_t a01, b01, a23, b23;
-            buf_chain_pairs(A, B, stage, lut, a01, b01);
-            buf_chain_pairs(A, B, stage, lut, a23, b23);
-            wa[q] = join_halves(a01, a23);
-            wb[q] = join_halves(b01, b23);
-        }
-    } else {
-        Chain A{ra};
-        Chain B{rb};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t a01 = chain_pair(A, stage, lut);
-            const uint32_t b01 = chain_pair(B, stage, lut);
-            const uint32_t a23 = chain_pair(A, stage, lut);
-            const uint32_t b23 = chain_pair(B, stage, lut);
-            wa[q] = join_halves(a01, a23);
-            wb[q] = join_halves(b01, b23);
-        }
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t a01 = chain_pair(A, stage, lut);
+        const uint32_t b01 = chain_pair(B, stage, lut);
+        const uint32_t a23 = chain_pair(A, stage, lut);
+        const uint32_t b23 = chain_pair(B, stage, lut);
+        wa[q] = join_halves(a01, a23);
+        wb[q] = join_halves(b01, b23);
     }
     wave_sync();  // every lane is done reading the staged words
     uint4 *pa = reinterpret_cast<uint4 *>(stage + lane * 8);
@@ -455,8 +444,9 @@ __device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, co
     wave_sync();
 }
 
-// decode_exponents with the buffered chains advanced through the pair
-// table (same clamping, same result).
+// decode_exponents with buffered chains advanced through the pair table
+// (same clamping, same result); the buffered chains' read ahead (one word
+// past the window) stays at index >= 0 for the same reason.
 __device__ inline void decode_exponents_paired(const ChunkGeom &g, const Gaps &gaps, const uint32_t *plut,
                                                uint32_t *stage, int lane) {
     constexpr uint32_t kMaxStart = 32 * (kRev - 13);
