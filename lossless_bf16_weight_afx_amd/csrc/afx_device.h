@@ -289,19 +289,31 @@ __device__ inline uint32_t complete_entry(uint32_t e, uint32_t e2) {
     return (e & 0xFF00u) | ((e2 & 0xFF00u) << 8) | ((e & 0xFFu) + ((e2 >> 24) & 0xFu));
 }
 
-// The buffered chains (BufChain) advanced through the pair table. Both
-// chains' table reads are issued before the (rare) branch that completes
-// entries holding one code, so that their latencies overlap. ea, eb: the
-// entries (byte 0: bits consumed; bytes 1, 2: the two symbols).
+// The paired chains run kLead bits behind the code they decode: their
+// 32-bit window starts with kLead bits already consumed (or, at a chunk's
+// first bit, the pad word above the staged words), so that the next 12
+// code bits sit at bits 29..18 of the window, and the pair table's byte
+// address (index times 4) is the window's high half-word masked: one
+// instruction.
+constexpr uint32_t kLead = 2;
+static_assert(kMaxLen + kLead + 2 == 16, "the table address is a masked high half-word");
+__device__ inline uint32_t pair_read(const uint32_t *plut, uint32_t win) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(plut) + ((win >> 16) & 0x3FFCu));
+}
+
+// The buffered chains (BufChain, kLead bits behind) advanced through the
+// pair table. Both chains' table reads are issued before the (rare) branch
+// that completes entries holding one code, so that their latencies overlap.
+// ea, eb: the entries (byte 0: bits consumed; bytes 1, 2: the two symbols).
 __device__ inline void pair_chain_steps(BufChain &a, BufChain &b, const uint32_t *stage, const uint32_t *plut,
                                         uint32_t &ea, uint32_t &eb) {
     const uint32_t wa = __builtin_amdgcn_alignbit(a.hi, a.lo, a.r);
     const uint32_t wb = __builtin_amdgcn_alignbit(b.hi, b.lo, b.r);
-    ea = plut[wa >> (32 - kMaxLen)];
-    eb = plut[wb >> (32 - kMaxLen)];
+    ea = pair_read(plut, wa);
+    eb = pair_read(plut, wb);
     if ((int32_t)(ea & eb) >= 0) {  // some entry holds one code: read the second
-        const uint32_t fa = plut[(wa << (ea & 31)) >> (32 - kMaxLen)];
-        const uint32_t fb = plut[(wb << (eb & 31)) >> (32 - kMaxLen)];
+        const uint32_t fa = pair_read(plut, wa << (ea & 31));
+        const uint32_t fb = pair_read(plut, wb << (eb & 31));
         ea = (int32_t)ea >= 0 ? complete_entry(ea, fa) : ea;
         eb = (int32_t)eb >= 0 ? complete_entry(eb, fb) : eb;
     }
@@ -446,12 +458,15 @@ __device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, co
 
 // decode_exponents with buffered chains advanced through the pair table
 // (same clamping, same result); the buffered chains' read ahead (one word
-// past the window) stays at index >= 0 for the same reason.
+// past the window) stays at index >= 0 for the same reason, and their
+// windows (kLead bits behind) at most reach the pad word above.
 __device__ inline void decode_exponents_paired(const ChunkGeom &g, const Gaps &gaps, const uint32_t *plut,
                                                uint32_t *stage, int lane) {
     constexpr uint32_t kMaxStart = 32 * (kRev - 13);
-    const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart);
-    const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart);
+    // kLead bits behind the chain start: at most at bit 32 kRev + kLead,
+    // whose window's high word is the pad word above the staged words
+    const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart) + kLead;
+    const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart) + kLead;
     uint32_t wa[8], wb[8];
     BufChain A = buf_chain(stage, ra), B = buf_chain(stage, rb);
 #pragma unroll
