@@ -87,11 +87,54 @@ __device__ inline void load_signmant(const TensorDesc &T, uint64_t lc, int lane,
     }
 }
 
+// Add the products of the lane's 8 values of one round (elements i..i+7 of
+// the chunk, columns col..col+7 of one row) with x into acc[m], token m.
+template <int M>
+__device__ inline void round_products(const GemvArgs &a, const uint16_t *xs, bool x_in_lds,
+                                      const __amdgpu_buffer_rsrc_t (&xrow)[M], uint2 b, const uint8_t *exb,
+                                      const uint8_t *sm, uint32_t i, uint32_t ne, uint32_t col, float (&acc)[M]) {
+    if (i + 8 <= ne) {
+        const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
+        // restored values as BF16 pairs (element 2q in the low half),
+        // multiplied two at a time against x's pairs
+        uint32_t p01, p23, p45, p67;
+        join4(b.x, e.x, p01, p23);
+        join4(b.y, e.y, p45, p67);
+        const bf16x2 w01 = bf16_pair(p01), w23 = bf16_pair(p23), w45 = bf16_pair(p45), w67 = bf16_pair(p67);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            // The staged copy is read with an LDS load and x in L2 with a
+            // buffer load: as two plain loads, the compiler merges them into
+            // one generic (flat) load of a selected pointer, which waits on
+            // both memory counters.
+            uint4 xv;
+            if (x_in_lds) {
+                xv = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * a.cols + col);
+            } else {
+                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xrow[m], 2 * col, 0, 0);
+                xv = make_uint4(t.x, t.y, t.z, t.w);
+            }
+            float s = __builtin_amdgcn_fdot2_f32_bf16(w01, bf16_pair(xv.x), acc[m], false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(w23, bf16_pair(xv.y), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(w45, bf16_pair(xv.z), s, false);
+            acc[m] = __builtin_amdgcn_fdot2_f32_bf16(w67, bf16_pair(xv.w), s, false);
+        }
+    } else {  // the matrix's last, partial round
+        for (uint32_t j = i; j < ne && j < i + 8; ++j) {
+            const uint32_t bb = sm[j], ee = exb[j];
+            const float w = __uint_as_float((((bb & 0x80u) << 8) | (ee << 7) | (bb & 0x7Fu)) << 16);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                acc[m] = fmaf(w, __uint_as_float((uint32_t)a.x[(uint64_t)m * a.cols + col + (j - i)] << 16), acc[m]);
+        }
+    }
+}
+
 // Restore chunk lc of W and add its products with x into y. smv holds (or
 // is receiving) chunk lc's sign/mantissa bytes on entry; as soon as they
 // have been used, the bytes of chunk next_lc (if any) are requested into it,
 // so that their latency overlaps the rest of this chunk and the next decode.
-template <int M>
+template <int M, bool kLong>
 __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_in_lds, uint64_t lc, uint2 (&smv)[8],
                                   bool has_next, uint64_t next_lc, const ChunkGeom &g, const Gaps &gaps,
                                   const uint32_t *plut, uint32_t *stage, int lane, uint64_t later_bases,
@@ -114,6 +157,47 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
     for (int m = 0; m < M; ++m)
         xrow[m] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.x + (uint64_t)m * a.cols), (short)0,
                                                     (int)(2 * a.cols), kBufferFlags);
+    if constexpr (kLong) {  // cols >= kChunk
+        // The chunk spans at most two rows: each lane's rounds lie in row
+        // row0 until its columns wrap, then in row0 + 1. The products go
+        // straight into one accumulator per row and token.
+        float a0[M], a1[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) a0[m] = a1[m] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
+            const uint32_t c = c0 + i;
+            const bool next_row = c >= a.cols;
+            const uint32_t col = next_row ? c - a.cols : c;
+            float t[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) t[m] = next_row ? a1[m] : a0[m];
+            round_products<M>(a, xs, x_in_lds, xrow, smv[r], exb, sm, i, ne, col, t);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                a0[m] = next_row ? a0[m] : t[m];
+                a1[m] = next_row ? t[m] : a1[m];
+            }
+        }
+        if (has_next) load_signmant(T, next_lc, lane, smv);
+        // Sum each row's products over the wave and add them into y.
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float s = wave_sum_to_lane63(a0[m]);
+            if (lane == kWave - 1) atomicAdd(a.y + (uint64_t)m * a.rows + row0, s);
+        }
+        if (c0 + ne > a.cols) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float s = wave_sum_to_lane63(a1[m]);
+                if (lane == kWave - 1) atomicAdd(a.y + (uint64_t)m * a.rows + row0 + 1, s);
+            }
+        }
+        return;
+    }
+    // Any row length: keep each round's products apart and sum them per
+    // row at the end.
     float acc[8][M];
     uint32_t drow[8];
 #pragma unroll
@@ -125,44 +209,7 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
         drow[r] = d;
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-        if (i + 8 <= ne) {
-            const uint2 b = smv[r];
-            const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
-            // restored values as BF16 pairs (element 2q in the low half),
-            // multiplied two at a time against x's pairs
-            uint32_t p01, p23, p45, p67;
-            join4(b.x, e.x, p01, p23);
-            join4(b.y, e.y, p45, p67);
-            const bf16x2 w01 = bf16_pair(p01), w23 = bf16_pair(p23), w45 = bf16_pair(p45), w67 = bf16_pair(p67);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                // The staged copy is read with an LDS load and x in L2 with
-                // a buffer load: as two plain loads, the compiler merges
-                // them into one generic (flat) load of a selected pointer,
-                // which waits on both memory counters.
-                uint4 xv;
-                if (x_in_lds) {
-                    xv = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * a.cols + col);
-                } else {
-                    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xrow[m], 2 * col, 0, 0);
-                    xv = make_uint4(t.x, t.y, t.z, t.w);
-                }
-                float s = __builtin_amdgcn_fdot2_f32_bf16(w01, bf16_pair(xv.x), 0.f, false);
-                s = __builtin_amdgcn_fdot2_f32_bf16(w23, bf16_pair(xv.y), s, false);
-                s = __builtin_amdgcn_fdot2_f32_bf16(w45, bf16_pair(xv.z), s, false);
-                s = __builtin_amdgcn_fdot2_f32_bf16(w67, bf16_pair(xv.w), s, false);
-                acc[r][m] = s;
-            }
-        } else {
-            for (uint32_t j = i; j < ne && j < i + 8; ++j) {
-                const uint32_t bb = sm[j], ee = exb[j];
-                const float w = __uint_as_float((((bb & 0x80u) << 8) | (ee << 7) | (bb & 0x7Fu)) << 16);
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    acc[r][m] = fmaf(w, __uint_as_float((uint32_t)a.x[(uint64_t)m * a.cols + col + (j - i)] << 16),
-                                     acc[r][m]);
-            }
-        }
+        round_products<M>(a, xs, x_in_lds, xrow, smv[r], exb, sm, i, ne, col, acc[r]);
     }
     if (has_next) load_signmant(T, next_lc, lane, smv);
     // Sum each row's products over the wave and add them into y.
@@ -192,7 +239,11 @@ struct GemvLds {
     uint32_t next_j;  // the workgroup's next unclaimed chunk of the matrix
 };
 
-template <int M>
+// kLong: every matrix of the batch has rows of a chunk or longer (cols >=
+// 4096), so a chunk spans at most two rows and the products need only two
+// accumulators per token (the general kernel keeps one per round and spills
+// registers at m = 4).
+template <int M, bool kLong>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void afx_gemv_kernel(const GemvBatch batch) {
     __shared__ __attribute__((aligned(16))) GemvLds lds;
@@ -268,7 +319,7 @@ void afx_gemv_kernel(const GemvBatch batch) {
                 if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
             }
             ChunkGeom gnn;
-            gemv_chunk<M>(a, xs, x_in_lds, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, plut, my_stage,
+            gemv_chunk<M, kLong>(a, xs, x_in_lds, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, plut, my_stage,
                           lane, bases_nn, gnn);
             if (!has_n) break;
             wave_sync();  // the exponent bytes have been read
@@ -284,21 +335,21 @@ void afx_gemv_kernel(const GemvBatch batch) {
     }
 }
 
-std::atomic<int> g_gemv_blocks[64];
-
-template <int M>
+template <int M, bool kLong>
 int gemv_max_blocks(int *out) {
+    static std::atomic<int> blocks[64];  // per device, for this kernel
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return AFX_E_HIP;
     if (dev < 0 || dev >= 64) return AFX_E_UNSUPPORTED;
-    int v = g_gemv_blocks[dev].load(std::memory_order_relaxed);
+    int v = blocks[dev].load(std::memory_order_relaxed);
     if (v <= 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return AFX_E_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, afx_gemv_kernel<M>, kThreads, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, afx_gemv_kernel<M, kLong>, kThreads, 0) !=
+            hipSuccess)
             return AFX_E_HIP;
         v = std::max(1, cus) * std::max(1, per_cu);
-        g_gemv_blocks[dev].store(v, std::memory_order_relaxed);
+        blocks[dev].store(v, std::memory_order_relaxed);
     }
     *out = v;
     return AFX_OK;
@@ -306,8 +357,8 @@ int gemv_max_blocks(int *out) {
 
 // One launch for up to kMaxGemvJobs checked matrices: the grid is split
 // among them in proportion to their chunk counts, as for a restore batch.
-template <int M>
-int launch_gemv(GemvBatch &batch, hipStream_t stream) {
+template <int M, bool kLong>
+int launch_gemv_kernel(GemvBatch &batch, hipStream_t stream) {
     uint64_t total = 0, first[kMaxGemvJobs];
     for (uint32_t t = 0; t < batch.n; ++t) {
         first[t] = total;
@@ -315,7 +366,7 @@ int launch_gemv(GemvBatch &batch, hipStream_t stream) {
     }
     if (total == 0) return AFX_OK;
     int max_blocks = 0;
-    const int rc = gemv_max_blocks<M>(&max_blocks);
+    const int rc = gemv_max_blocks<M, kLong>(&max_blocks);
     if (rc != AFX_OK) return rc;
     const uint64_t per_block = (total + max_blocks - 1) / max_blocks;
     const uint64_t grid = std::max<uint64_t>(1, (total + per_block - 1) / per_block);
@@ -327,10 +378,17 @@ int launch_gemv(GemvBatch &batch, hipStream_t stream) {
         batch.j[t].t.blk_hi = (uint32_t)hi;
     }
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
-    return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemv_kernel<M>), dim3((unsigned)grid),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemv_kernel<M, kLong>), dim3((unsigned)grid),
                            dim3(kThreads), args, 0, stream) == hipSuccess
                ? AFX_OK
                : AFX_E_HIP;
+}
+
+template <int M>
+int launch_gemv(GemvBatch &batch, hipStream_t stream) {
+    bool all_long = true;
+    for (uint32_t t = 0; t < batch.n; ++t) all_long &= batch.j[t].cols >= kChunk;
+    return all_long ? launch_gemv_kernel<M, true>(batch, stream) : launch_gemv_kernel<M, false>(batch, stream);
 }
 
 int check_gemv_job(const afx_gemv_job &j, uint32_t m) {

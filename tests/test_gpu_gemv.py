@@ -102,3 +102,31 @@ def test_batch_of_mixed_matrices_one_launch():
     for (info, db, xd, y), (ref, bound), shape in zip(keep, refs, shapes):
         err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
         assert np.all(err <= bound), shape
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_batch_of_long_rows(m):
+    """A batch whose matrices all have rows of a chunk or longer (the two-
+    accumulator kernel): rows that wrap at odd columns (8200), a last chunk
+    of 104 elements (a partial round), rows of exactly one chunk and
+    down_proj-length rows; every product within its bound."""
+    shapes = [(40, 5120), (9, 4096), (13, 8200), (3, 17408)]
+    rng = np.random.default_rng(47 + m)
+    jobs, keep, refs = [], [], []
+    for t, (rows, cols) in enumerate(shapes):
+        w = synth.generate(synth.TensorSpec(f"l{t}", (rows, cols), "t4" if t == 2 else "normal", 900 + t))
+        blob = oracle.encode(w, (rows, cols))
+        info = afx.afx_query(blob)
+        db = afx.to_device(blob)
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, cols)).astype(np.float32))
+        xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+        y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+        keep.append((info, db, xd, y))
+        jobs.append((info, db.data_ptr(), rows, cols, xd.data_ptr(), y.data_ptr()))
+        refs.append(oracle.restore_gemv(blob, rows, cols, x, threads=4))
+    say(f"[gpu] case gemv batch of 4 long-row matrices, m={m}")
+    afx.afx_restore_gemv_batch_async(jobs, m, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for (info, db, xd, y), (ref, bound), shape in zip(keep, refs, shapes):
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound), shape
