@@ -48,7 +48,7 @@ struct Batch {
 // sign/mantissa bytes, store. `stage` holds the chunk's code words on entry
 // and is free (but for the exponent bytes just written) on exit.
 __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const ChunkGeom &g, const Gaps &gaps,
-                                     const uint16_t *lut, uint32_t *stage, int lane, uint64_t later_bases,
+                                     const uint32_t *plut, uint32_t *stage, int lane, uint64_t later_bases,
                                      ChunkGeom &later) {
     const uint64_t e0 = lc * kChunk;
     const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
@@ -65,7 +65,7 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
         smv[r] = make_uint2(t.x, t.y);  // tail elements are reread below
     }
 
-    decode_exponents(g, gaps, lut, stage, lane);
+    decode_exponents_paired(g, gaps, plut, stage, lane);
     // Read out the bases fetched for a later chunk now, while the only loads
     // issued after them are this chunk's sign/mantissa bytes (needed next
     // anyway): read after the stores below, they would make the wave wait
@@ -102,13 +102,14 @@ void afx_decode_kernel(const Batch batch) {
     // The workgroup's LDS as one object, the decode table first: at LDS
     // address 0 a table read needs no base added to its index.
     struct Lds {
-        uint16_t lut[kLutEntries];                  // 8 KB
+        uint32_t plut[kLutEntries];                 // 16 KB
         uint32_t stage[kWavesPerBlock][kStageRow];  // 98 KB
         LutScratch scratch;
         uint32_t next_j;  // the workgroup's next unclaimed chunk of the tensor
     };
     __shared__ __attribute__((aligned(16))) Lds lds;
-    uint16_t *lut = lds.lut;
+    uint32_t *plut = lds.plut;
+    uint16_t *lut = reinterpret_cast<uint16_t *>(&lds.stage[0][0]);  // the one-code table, while building
     auto &stage = lds.stage;
     LutScratch &scratch = lds.scratch;
     uint32_t &next_j = lds.next_j;
@@ -154,8 +155,10 @@ void afx_decode_kernel(const Batch batch) {
         }
         __syncthreads();  // every wave is done with the previous table and counter
         if (threadIdx.x == 0) next_j = 2 * kWavesPerBlock;
-        build_lut(len, lut, scratch);  // ends with a barrier
+        build_lut(len, lut, scratch);
         __syncthreads();
+        build_pair_lut(lut, plut);
+        __syncthreads();  // the pair table is complete and the staging area free
         if (!has_c) continue;
         put_stream(T, g, s, my_stage, lane);
         wave_sync();
@@ -181,7 +184,7 @@ void afx_decode_kernel(const Batch batch) {
                 if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
             }
             ChunkGeom gnn;
-            restore_chunk(T, k + (uint64_t)jc * nb, g, gaps, lut, my_stage, lane, bases_nn, gnn);
+            restore_chunk(T, k + (uint64_t)jc * nb, g, gaps, plut, my_stage, lane, bases_nn, gnn);
             if (!has_n) break;
             wave_sync();  // the exponent bytes have been read
             put_stream(T, gn, sn, my_stage, lane);
