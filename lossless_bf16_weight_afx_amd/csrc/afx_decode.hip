@@ -65,7 +65,7 @@ __device__ inline void restore_chunk(const TensorDesc &T, uint64_t lc, const Chu
         smv[r] = make_uint2(t.x, t.y);  // tail elements are reread below
     }
 
-    decode_exponents_paired(g, gaps, plut, stage, lane);
+    decode_exponents(g, gaps, plut, stage, lane);
     // Read out the bases fetched for a later chunk now, while the only loads
     // issued after them are this chunk's sign/mantissa bytes (needed next
     // anyway): read after the stores below, they would make the wave wait

@@ -186,35 +186,15 @@ __device__ inline uint32_t sym_pair(uint32_t e1, uint32_t e2) { return __builtin
 // Bytes 0,1 of lo and of hi as the four bytes of a word.
 __device__ inline uint32_t join_halves(uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x05040100u); }
 
+__device__ inline uint32_t lookup(const uint16_t *lut, uint32_t win) { return lut[win >> (32 - kMaxLen)]; }
+
 // One decoding chain. With P the bit position in the staged words (MSB
 // first), the chain keeps r = 32 * kRev - P. Then the next 32 stream bits are
 // the funnel shift of staged words [r/32 + 1] (high) and [r/32] (low) by
-// r mod 32, and consuming a code of length l is r -= l.
-struct Chain {
-    uint32_t r;
-};
-
-__device__ inline uint32_t window(const uint32_t *stage, uint32_t r) {
-    const uint32_t *p = stage + (r >> 5);
-    return __builtin_amdgcn_alignbit(p[1], p[0], r);
-}
-
-__device__ inline uint32_t lookup(const uint16_t *lut, uint32_t win) { return lut[win >> (32 - kMaxLen)]; }
-
-// Decode two symbols from one 32-bit window (two codes take at most 24 bits)
-// and return them as bytes 0,1.
-__device__ inline uint32_t chain_pair(Chain &c, const uint32_t *stage, const uint16_t *lut) {
-    const uint32_t win = window(stage, c.r);
-    const uint32_t e1 = lookup(lut, win);
-    const uint32_t e2 = lookup(lut, win << (e1 & 31));
-    c.r -= (e1 + e2) & 0xFF;
-    return sym_pair(e1, e2);
-}
-
-// The same chain with the two staged words of its window and the word after
-// them kept in registers: the next word is read one step ahead, so forming a
-// window never waits for LDS. Two such chains advance together (see
-// pair_chain_steps) so that their table reads overlap.
+// r mod 32, and consuming a code of length l is r -= l. The two staged words
+// of the window and the word after them are kept in registers, the next word
+// read one step ahead, so forming a window never waits for LDS. Two chains
+// advance together so that their table reads overlap.
 struct BufChain {
     uint32_t r, q, hi, lo, nx;  // q = r / 32: hi, lo, nx are staged words q + 1, q, q - 1
 };
@@ -253,9 +233,8 @@ __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t 
     sb = sym_pair(b1, b2);
 }
 
-// A second table over the same 12-bit windows, for kernels whose decode
-// is bound by instruction issue and LDS rather than by HBM. Entry i
-// (32 bits) describes the codes that start window i:
+// A second table over the same 12-bit windows, built from the first. Entry
+// i (32 bits) describes the codes that start window i:
 //   byte 0   bits to consume: both codes' lengths when the second code also
 //            ends inside the window, else the first code's length;
 //   byte 1   the first code's symbol;
@@ -263,7 +242,9 @@ __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t 
 //   byte 3   bits 0-3: the first code's length; bit 7: both codes fit.
 // With mean code lengths near 2.6 bits, two codes fit in 12 bits for about
 // 99.6% of windows, so most two-symbol steps take one table read instead of
-// two dependent ones.
+// two dependent ones. The restore and the matrix-vector kernel decode
+// through it: the restore's first and last chunks, and all of the fused
+// kernel's, are bound by the decode.
 constexpr uint32_t kPairBit = 0x80000000u;
 
 // Fill the pair table from the one-code table (both in LDS); all kNThreads
@@ -423,44 +404,14 @@ __device__ inline void store_out(uint16_t *p, uint4 v) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
 }
 
-// Decode a staged chunk's 4096 exponent codes and leave the exponent bytes
-// in element order at the start of `stage` (which held the code words).
-// Chain starts are clamped so that 32 decodes (at most 384 bits) never leave
-// the staged words even on a corrupt gap. Plain chains: the choice of a
-// kernel bound by HBM; decode_exponents_paired below is the one for kernels
-// whose chunk time the decode bounds.
-__device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, const uint16_t *lut, uint32_t *stage,
-                                        int lane) {
-    constexpr uint32_t kMaxStart = 32 * (kRev - 13);
-    const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart);
-    const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart);
-    uint32_t wa[8], wb[8];
-    Chain A{ra};
-    Chain B{rb};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const uint32_t a01 = chain_pair(A, stage, lut);
-        const uint32_t b01 = chain_pair(B, stage, lut);
-        const uint32_t a23 = chain_pair(A, stage, lut);
-        const uint32_t b23 = chain_pair(B, stage, lut);
-        wa[q] = join_halves(a01, a23);
-        wb[q] = join_halves(b01, b23);
-    }
-    wave_sync();  // every lane is done reading the staged words
-    uint4 *pa = reinterpret_cast<uint4 *>(stage + lane * 8);
-    uint4 *pb = reinterpret_cast<uint4 *>(stage + (lane + kWave) * 8);
-    pa[0] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-    pa[1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
-    pb[0] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
-    pb[1] = make_uint4(wb[4], wb[5], wb[6], wb[7]);
-    wave_sync();
-}
-
-// decode_exponents with buffered chains advanced through the pair table
-// (same clamping, same result); the buffered chains' read ahead (one word
-// past the window) stays at index >= 0 for the same reason, and their
-// windows (kLead bits behind) at most reach the pad word above.
-__device__ inline void decode_exponents_paired(const ChunkGeom &g, const Gaps &gaps, const uint32_t *plut,
+// Decode a staged chunk's 4096 exponent codes through the pair table and
+// leave the exponent bytes in element order at the start of `stage` (which
+// held the code words). Chain starts are clamped so that 32 decodes (at most
+// 384 bits) never leave the staged words even on a corrupt gap; the chains'
+// read ahead (one word past the window) stays at index >= 0 for the same
+// reason, and their windows (kLead bits behind) at most reach the pad word
+// above.
+__device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, const uint32_t *plut,
                                                uint32_t *stage, int lane) {
     constexpr uint32_t kMaxStart = 32 * (kRev - 13);
     // kLead bits behind the chain start: at most at bit 32 kRev + kLead,

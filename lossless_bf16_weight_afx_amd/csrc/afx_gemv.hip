@@ -143,7 +143,7 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
     const uint64_t e0 = lc * kChunk;
     const uint32_t ne = (uint32_t)umin64(kChunk, T.n - e0);
     const uint8_t *sm = T.signmant + e0;
-    decode_exponents_paired(g, gaps, plut, stage, lane);
+    decode_exponents(g, gaps, plut, stage, lane);
     asm volatile("" : "+v"(later_bases));  // not before the decode above
     later = geom_from_lanes(later_bases);
 
