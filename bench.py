@@ -474,7 +474,7 @@ def bench_token(args, threads: int) -> int:
     token's activations (m = 1, 2 or 4 rows), straight from the compressed
     model resident in HBM with the fused matrix-vector kernel, one batch call
     per unit. Compared with the same products on the BF16 model resident in
-    HBM (torch.mm) and with restoring each unit into one scratch buffer
+    HBM (torch.mm, and torch.mv at m = 1) and with restoring each unit into one scratch buffer
     before its products. The embedding lookup reads one row and is left out.
     The activations are synthetic; nothing between the products (attention,
     norms) is computed: this times the weight pass the pages' per-token
@@ -552,7 +552,12 @@ def bench_token(args, threads: int) -> int:
         for (sp, _, _, _), w in zip(mats, wbf):
             torch.mm(x_for(sp.shape[1]), w.t())
 
+    def mv(k):  # torch's matrix-vector path, for one token
+        for (sp, _, _, _), w in zip(mats, wbf):
+            torch.mv(w, x_for(sp.shape[1])[0])
+
     ms_mm = _time_steps(stream_, mm, args.steps, args.warmup)
+    ms_mv = _time_steps(stream_, mv, args.steps, args.warmup) if m == 1 else None
     del wbf
     torch.cuda.empty_cache()
     # restore each unit into one scratch buffer (256-byte aligned outputs),
@@ -589,7 +594,8 @@ def bench_token(args, threads: int) -> int:
                    "bf16_bytes": 2 * n_weights, "launches": len(per_unit)},
         "within_bound": bool(within),
         "token_pass_ms": {"fused_from_compressed": round(ms_fused, 3), "bf16_resident_torch_mm": round(ms_mm, 3),
-                          "restore_each_unit_then_torch_mm": round(ms_rmm, 3)},
+                          "restore_each_unit_then_torch_mm": round(ms_rmm, 3),
+                          **({"bf16_resident_torch_mv": round(ms_mv, 3)} if ms_mv is not None else {})},
         "hbm_weight_bytes": {"compressed": blob_total, "bf16": 2 * n_weights},
         "roofline": {"bound": "hbm", "achieved": round(blob_total / (ms_fused * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
