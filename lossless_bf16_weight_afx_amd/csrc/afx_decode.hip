@@ -18,18 +18,20 @@
 //     different speeds; claiming keeps them finishing together;
 //   * for every tensor it serves, the workgroup builds the 4096-entry decode
 //     table (u16: symbol << 8 | length) of that tensor's canonical code in
-//     LDS, from the 256 code lengths alone;
+//     LDS, from the 256 code lengths alone, and from it the pair table (u32:
+//     both codes that start a 12-bit window when both fit in it);
 //   * each wave restores one chunk at a time, software-pipelined: while chunk
 //     i decodes, the code words and gap offsets of chunk i + 1 and the bit
 //     bases of chunk i + 2 are in flight. The code words are staged in the
 //     wave's own LDS slice; lane j then decodes groups j and j + 64 (32
 //     symbols each, two independent dependency chains), two symbols per
-//     32-bit window of the staged stream;
+//     32-bit window of the staged stream, mostly with one pair-table read;
 //   * decoded exponent bytes go back to the wave's LDS slice in element order;
 //     the wave re-reads them in store order, merges them with the
 //     sign/mantissa bytes and writes 16-byte stores, 1 KB per instruction.
 // There is no floating point and no matrix work: the kernel is bound by HBM
-// bytes and by the serial table-lookup chain of each lane.
+// bytes, and its first and last chunks by the serial table-lookup chain of
+// each lane.
 #include <hip/hip_runtime.h>
 
 #include <atomic>

@@ -19,9 +19,10 @@
 // addition), then across the wave, then into y with atomic adds (in no fixed
 // order).
 //
-// Work decomposition as in the restore: one 16-wave workgroup per CU, chunks
-// round the workgroups, claimed one at a time by the waves from an LDS
-// counter, code words staged a chunk ahead.
+// Work decomposition and decode as in the restore: one 16-wave workgroup per
+// CU, chunks round the workgroups, claimed one at a time by the waves from an
+// LDS counter, code words staged a chunk ahead, decoded through the pair
+// table.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
