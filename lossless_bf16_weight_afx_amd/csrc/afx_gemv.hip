@@ -273,12 +273,18 @@ void afx_gemv_kernel(const GemvBatch batch) {
         uint32_t jc = wave, jn = wave + kWavesPerBlock;
         const bool has_c = jc < mine;
         bool has_n = jn < mine;
-        const uint32_t len = wave < kSymbolWaves ? T.code_len[threadIdx.x] : 0;
-        uint64_t bases_c = 0, bases_n = 0;
-        Gaps gaps{0, 0};
-        if (has_c) bases_c = load_bases(T, k + (uint64_t)jc * nb, lane);
-        if (has_n) bases_n = load_bases(T, k + (uint64_t)jn * nb, lane);
-        if (has_c) gaps = load_gaps(T, k + (uint64_t)jc * nb, lane);
+        // Every thread loads a code length (threads past 255 repeat some), so
+        // that no branch around the load makes the compiler wait for it
+        // before the bases below are requested; only waves 0-3 pass theirs on.
+        const uint32_t len_any = T.code_len[threadIdx.x & 255];
+        // Unconditional loads (of chunk k, which exists, for a wave without
+        // such a chunk): around a branch, the compiler's wait at the join
+        // would hold the bases back until the code lengths arrive.
+        const uint64_t lc_c = k + (uint64_t)(has_c ? jc : 0u) * nb;
+        const uint64_t lc_n = k + (uint64_t)(has_n ? jn : 0u) * nb;
+        uint64_t bases_c = load_bases(T, lc_c, lane);
+        uint64_t bases_n = load_bases(T, lc_n, lane);
+        Gaps gaps = load_gaps(T, lc_c, lane);
         ChunkGeom g{};
         StreamRegs s;
         if (has_c) {
@@ -293,7 +299,7 @@ void afx_gemv_kernel(const GemvBatch batch) {
         if (x_in_lds)
             for (uint32_t i = threadIdx.x; i < xbytes / 16; i += kThreads)
                 reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(a.x)[i];
-        build_lut(len, lut, scratch);
+        build_lut(wave < kSymbolWaves ? len_any : 0u, lut, scratch);
         __syncthreads();
         build_pair_lut(lut, plut);
         __syncthreads();  // the pair table is complete and the staging area free
