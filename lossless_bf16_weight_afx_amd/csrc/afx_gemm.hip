@@ -210,8 +210,10 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t t0 = blockIdx.y * (kSplit ? 32 : kGemmWaves * 32 * kTB);
     const uint32_t m = batch.m;
 
-    build_lut<kGemmThreads>(T.code_len[threadIdx.x], lut, scratch);
-    __syncthreads();
+    // The code lengths and the first slabs' bit offsets are requested
+    // together, then the first slab's words (which need the offsets); the
+    // table is built while those are in flight.
+    const uint32_t len = T.code_len[threadIdx.x];
 
     // Restore: this lane's row (one quad per row) and its two groups.
     const uint32_t q4 = (uint32_t)lane & 3;
@@ -240,9 +242,11 @@ void afx_gemm_kernel(const GemmBatch batch) {
     // dependent round trips (offsets, then the words they point at) stay off
     // the path of every slab but the first.
     SlabBits bits_c = slab_bits(T, row_e + kbeg, q4);
-    SlabData data_c = slab_data(T, row_e + kbeg, q4, bits_c);
     const bool two = kbeg + kSlabCols < kend;
-    SlabBits bits_n = two ? slab_bits(T, row_e + kbeg + kSlabCols, q4) : bits_c;
+    SlabBits bits_n = slab_bits(T, row_e + kbeg + (two ? kSlabCols : 0u), q4);
+    SlabData data_c = slab_data(T, row_e + kbeg, q4, bits_c);
+    build_lut<kGemmThreads>(len, lut, scratch);
+    __syncthreads();
     f32x16 acc[kB][2];
 #pragma unroll
     for (int tb = 0; tb < kB; ++tb) acc[tb][0] = acc[tb][1] = f32x16{};
