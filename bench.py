@@ -712,7 +712,10 @@ def bench_disk(args, threads: int) -> int:
         log(f"[bench] checked pass over {sorted(check_idx)}: bit_exact={exact}")
         read_s = float(np.median([ds.read_only_s() for _ in range(max(1, min(args.steps, 3)))]))
         copy_s = float(np.median([ds.copy_only_s() for _ in range(3)]))
-        runs = [ds.run() for _ in range(max(1, args.steps))]
+        runs = []
+        for k in range(max(1, args.steps)):  # each pass takes seconds: report each
+            runs.append(ds.run())
+            log(f"[bench] pass {k + 1}/{max(1, args.steps)}: {runs[-1]['e2e_s']:.2f} s")
         e2e_s = float(np.median([r["e2e_s"] for r in runs]))
         dec_ms = float(np.median([sum(r["decode_ms"]) for r in runs]))
         b_disk = stored / read_s
@@ -750,7 +753,10 @@ def bench_disk(args, threads: int) -> int:
         exact_h = len(ok) == len(check_idx) and all(ok)
         log(f"[bench] checked host-unpack pass over {sorted(check_idx)}: bit_exact={exact_h}")
         t_unpack_host = float(np.median([hs.unpack_only_s(1) for _ in range(3)]))
-        hruns = [hs.run() for _ in range(max(1, args.steps))]
+        hruns = []
+        for k in range(max(1, args.steps)):
+            hruns.append(hs.run())
+            log(f"[bench] host-unpack pass {k + 1}/{max(1, args.steps)}: {hruns[-1]['e2e_s']:.2f} s")
         h_e2e = float(np.median([r["e2e_s"] for r in hruns]))
         line["host_unpack"] = {
             "pass_s": round(h_e2e, 2), "ready_weight_GBps": round(restored / h_e2e / 1e9, 2),
@@ -810,7 +816,10 @@ def bench_tiers(args, threads: int) -> int:
             ok = []
             tp.run(on_unit=lambda i, out: ok.append(store.check_unit(out, specs[i])) if i in check_idx else None)
             exact &= len(ok) == len(check_idx) and all(ok)
-            passes = [tp.run() for _ in range(max(1, args.steps))]
+            passes = []
+            for k in range(max(1, args.steps)):  # a pass can take seconds: report each
+                passes.append(tp.run())
+                log(f"[bench]   pass {k + 1}/{max(1, args.steps)}: {passes[-1]:.3f} s")
             pass_s = float(np.median(passes))
             counts = {t: tier.count(t) for t in tiers.TIERS}
             rows.append({"gpu_budget_GB": gpu_b / GB, "host_budget_GB": host_b / GB, "tiers": counts,
