@@ -88,11 +88,29 @@ __device__ inline void load_signmant(const TensorDesc &T, uint64_t lc, int lane,
     }
 }
 
-// Add the products of the lane's 8 values of one round (elements i..i+7 of
-// the chunk, columns col..col+7 of one row) with x into acc[m], token m.
+// x's 8 values at columns col..col+7 of each token row. The staged copy is
+// read with an LDS load and x in L2 with a buffer load: as two plain loads,
+// the compiler merges them into one generic (flat) load of a selected
+// pointer, which waits on both memory counters.
 template <int M>
-__device__ inline void round_products(const GemvArgs &a, const uint16_t *xs, bool x_in_lds,
-                                      const __amdgpu_buffer_rsrc_t (&xrow)[M], uint2 b, const uint8_t *exb,
+__device__ inline void load_x(const GemvArgs &a, const uint16_t *xs, bool x_in_lds,
+                              const __amdgpu_buffer_rsrc_t (&xrow)[M], uint32_t col, uint4 (&xv)[M]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (x_in_lds) {
+            xv[m] = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * a.cols + col);
+        } else {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xrow[m], 2 * col, 0, 0);
+            xv[m] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+    }
+}
+
+// Add the products of the lane's 8 values of one round (elements i..i+7 of
+// the chunk, columns col..col+7 of one row) with x (xv: those columns of
+// each token row) into acc[m], token m.
+template <int M>
+__device__ inline void round_products(const GemvArgs &a, const uint4 (&xv)[M], uint2 b, const uint8_t *exb,
                                       const uint8_t *sm, uint32_t i, uint32_t ne, uint32_t col, float (&acc)[M]) {
     if (i + 8 <= ne) {
         const uint2 e = *reinterpret_cast<const uint2 *>(exb + i);
@@ -104,21 +122,10 @@ __device__ inline void round_products(const GemvArgs &a, const uint16_t *xs, boo
         const bf16x2 w01 = bf16_pair(p01), w23 = bf16_pair(p23), w45 = bf16_pair(p45), w67 = bf16_pair(p67);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            // The staged copy is read with an LDS load and x in L2 with a
-            // buffer load: as two plain loads, the compiler merges them into
-            // one generic (flat) load of a selected pointer, which waits on
-            // both memory counters.
-            uint4 xv;
-            if (x_in_lds) {
-                xv = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * a.cols + col);
-            } else {
-                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xrow[m], 2 * col, 0, 0);
-                xv = make_uint4(t.x, t.y, t.z, t.w);
-            }
-            float s = __builtin_amdgcn_fdot2_f32_bf16(w01, bf16_pair(xv.x), acc[m], false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(w23, bf16_pair(xv.y), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(w45, bf16_pair(xv.z), s, false);
-            acc[m] = __builtin_amdgcn_fdot2_f32_bf16(w67, bf16_pair(xv.w), s, false);
+            float s = __builtin_amdgcn_fdot2_f32_bf16(w01, bf16_pair(xv[m].x), acc[m], false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(w23, bf16_pair(xv[m].y), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(w45, bf16_pair(xv[m].z), s, false);
+            acc[m] = __builtin_amdgcn_fdot2_f32_bf16(w67, bf16_pair(xv[m].w), s, false);
         }
     } else {  // the matrix's last, partial round
         for (uint32_t j = i; j < ne && j < i + 8; ++j) {
@@ -165,20 +172,33 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
         float a0[M], a1[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) a0[m] = a1[m] = 0.f;
+        // x of several rounds is requested together (16 registers), so
+        // that reads from L2 wait once per batch rather than once per round
+        constexpr int kBatch = M >= 4 ? 1 : 4 / M;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint32_t i = (uint32_t)r * (8 * kWave) + 8 * (uint32_t)lane;
-            const uint32_t c = c0 + i;
-            const bool next_row = c >= a.cols;
-            const uint32_t col = next_row ? c - a.cols : c;
-            float t[M];
+        for (int r0 = 0; r0 < 8; r0 += kBatch) {
+            uint4 xv[kBatch][M];
+            uint32_t col[kBatch];
+            bool next_row[kBatch];
 #pragma unroll
-            for (int m = 0; m < M; ++m) t[m] = next_row ? a1[m] : a0[m];
-            round_products<M>(a, xs, x_in_lds, xrow, smv[r], exb, sm, i, ne, col, t);
+            for (int q = 0; q < kBatch; ++q) {
+                const uint32_t c = c0 + (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
+                next_row[q] = c >= a.cols;
+                col[q] = next_row[q] ? c - a.cols : c;
+                load_x<M>(a, xs, x_in_lds, xrow, col[q], xv[q]);
+            }
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                a0[m] = next_row ? a0[m] : t[m];
-                a1[m] = next_row ? t[m] : a1[m];
+            for (int q = 0; q < kBatch; ++q) {
+                const uint32_t i = (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
+                float t[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m) t[m] = next_row[q] ? a1[m] : a0[m];
+                round_products<M>(a, xv[q], smv[r0 + q], exb, sm, i, ne, col[q], t);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    a0[m] = next_row[q] ? a0[m] : t[m];
+                    a1[m] = next_row[q] ? t[m] : a1[m];
+                }
             }
         }
         if (has_next) load_signmant(T, next_lc, lane, smv);
@@ -210,7 +230,9 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
         drow[r] = d;
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-        round_products<M>(a, xs, x_in_lds, xrow, smv[r], exb, sm, i, ne, col, acc[r]);
+        uint4 xv[M];
+        load_x<M>(a, xs, x_in_lds, xrow, col, xv);
+        round_products<M>(a, xv, smv[r], exb, sm, i, ne, col, acc[r]);
     }
     if (has_next) load_signmant(T, next_lc, lane, smv);
     // Sum each row's products over the wave and add them into y.
