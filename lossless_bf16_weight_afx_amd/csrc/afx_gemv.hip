@@ -138,6 +138,43 @@ __device__ inline void round_products(const GemvArgs &a, const uint4 (&xv)[M], u
     }
 }
 
+// The eight rounds of a chunk whose rows are a chunk or longer: each lane's
+// rounds lie in one row until its columns wrap, then in the next; the
+// products go into a0 (first row) or a1 (second), per token. x is requested
+// kBatch rounds at a time.
+template <int M, int kBatch>
+__device__ inline void long_rounds(const GemvArgs &a, const uint16_t *xs, bool x_in_lds,
+                                   const __amdgpu_buffer_rsrc_t (&xrow)[M], const uint2 (&smv)[8],
+                                   const uint8_t *exb, const uint8_t *sm, uint32_t ne, uint32_t c0, int lane,
+                                   float (&a0)[M], float (&a1)[M]) {
+#pragma unroll
+    for (int r0 = 0; r0 < 8; r0 += kBatch) {
+        uint4 xv[kBatch][M];
+        uint32_t col[kBatch];
+        bool next_row[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const uint32_t c = c0 + (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
+            next_row[q] = c >= a.cols;
+            col[q] = next_row[q] ? c - a.cols : c;
+            load_x<M>(a, xs, x_in_lds, xrow, col[q], xv[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const uint32_t i = (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
+            float t[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) t[m] = next_row[q] ? a1[m] : a0[m];
+            round_products<M>(a, xv[q], smv[r0 + q], exb, sm, i, ne, col[q], t);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                a0[m] = next_row[q] ? a0[m] : t[m];
+                a1[m] = next_row[q] ? t[m] : a1[m];
+            }
+        }
+    }
+}
+
 // Restore chunk lc of W and add its products with x into y. smv holds (or
 // is receiving) chunk lc's sign/mantissa bytes on entry; as soon as they
 // have been used, the bytes of chunk next_lc (if any) are requested into it,
@@ -172,35 +209,14 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
         float a0[M], a1[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) a0[m] = a1[m] = 0.f;
-        // x of several rounds is requested together (16 registers), so
-        // that reads from L2 wait once per batch rather than once per round
-        constexpr int kBatch = M >= 4 ? 1 : 4 / M;
-#pragma unroll
-        for (int r0 = 0; r0 < 8; r0 += kBatch) {
-            uint4 xv[kBatch][M];
-            uint32_t col[kBatch];
-            bool next_row[kBatch];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const uint32_t c = c0 + (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
-                next_row[q] = c >= a.cols;
-                col[q] = next_row[q] ? c - a.cols : c;
-                load_x<M>(a, xs, x_in_lds, xrow, col[q], xv[q]);
-            }
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const uint32_t i = (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
-                float t[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) t[m] = next_row[q] ? a1[m] : a0[m];
-                round_products<M>(a, xv[q], smv[r0 + q], exb, sm, i, ne, col[q], t);
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    a0[m] = next_row[q] ? a0[m] : t[m];
-                    a1[m] = next_row[q] ? t[m] : a1[m];
-                }
-            }
-        }
+        // x in L2: request x of several rounds together (16 registers),
+        // so that the reads wait once per batch rather than once per round.
+        // x staged in LDS: one round at a time (batched, the LDS reads
+        // conflicted more).
+        if (x_in_lds)
+            long_rounds<M, 1>(a, xs, true, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
+        else
+            long_rounds<M, (M >= 4 ? 1 : 4 / M)>(a, xs, false, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
         if (has_next) load_signmant(T, next_lc, lane, smv);
         // Sum each row's products over the wave and add them into y.
 #pragma unroll
