@@ -111,7 +111,6 @@ void afx_decode_kernel(const Batch batch) {
     };
     __shared__ __attribute__((aligned(16))) Lds lds;
     uint32_t *plut = lds.plut;
-    uint16_t *lut = reinterpret_cast<uint16_t *>(&lds.stage[0][0]);  // the one-code table, while building
     auto &stage = lds.stage;
     LutScratch &scratch = lds.scratch;
     uint32_t &next_j = lds.next_j;
@@ -163,10 +162,8 @@ void afx_decode_kernel(const Batch batch) {
         }
         __syncthreads();  // every wave is done with the previous table and counter
         if (threadIdx.x == 0) next_j = 2 * kWavesPerBlock;
-        build_lut(wave < kSymbolWaves ? len_any : 0u, lut, scratch);
-        __syncthreads();
-        build_pair_lut(lut, plut);
-        __syncthreads();  // the pair table is complete and the staging area free
+        build_lut<kThreads, true>(wave < kSymbolWaves ? len_any : 0u, plut, scratch);
+        __syncthreads();  // the pair table is complete
         if (!has_c) continue;
         put_stream(T, g, s, my_stage, lane);
         wave_sync();

@@ -78,17 +78,23 @@ __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Build the decode table of one canonical code: entry i (a 12-bit window of
-// the stream, MSB first) holds (symbol << 8) | length of the code word that
-// starts the window. The length sits in the low bits so that a 32-bit shift
-// by the whole entry consumes exactly the code (the hardware reads only the
-// low 5 bits of a shift amount). All kNThreads threads of the workgroup
-// (256 or more) take part: thread s < 256 owns symbol s and passes its code
-// length (the others pass 0), then every thread s fills table entries
-// [kPer s, kPer s + kPer), kPer = 4096 / kNThreads. Callers bracket it with
-// barriers.
-template <int kNThreads = kThreads>
-__device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
+// Bit 31 of a pair-table entry: both codes of the window fit in it (the
+// pair table is described with its reads below).
+constexpr uint32_t kPairBit = 0x80000000u;
+
+// Build a decode table of one canonical code over the 12-bit windows of the
+// stream (MSB first). !kPair: the one-code table, u16 entry i = (symbol <<
+// 8) | length of the code word that starts window i; the length sits in the
+// low bits so that a 32-bit shift by the whole entry consumes exactly the
+// code (the hardware reads only the low 5 bits of a shift amount). kPair:
+// the pair table (u32 entries, see pair_read), each entry computed from the
+// codes of window i and of the window shifted past its first code. All
+// kNThreads threads of the workgroup (256 or more) take part: thread s < 256
+// owns symbol s and passes its code length (the others pass 0), then every
+// thread s fills table entries [kPer s, kPer s + kPer), kPer = 4096 /
+// kNThreads. Callers bracket it with barriers.
+template <int kNThreads = kThreads, bool kPair = false>
+__device__ void build_lut(uint32_t len, void *table, LutScratch &S) {
     static_assert(kNThreads >= 256 && kLutEntries % (4 * kNThreads) == 0, "4-entry blocks per thread");
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1), wave = s / kWave;
@@ -149,6 +155,20 @@ __device__ void build_lut(uint32_t len, uint16_t *lut, LutScratch &S) {
         return ((uint32_t)S.sorted[j & 255] << 8) | l;
     };
     constexpr uint32_t kPer = kLutEntries / kNThreads;  // entries per thread
+    if constexpr (kPair) {
+        uint32_t *plut = static_cast<uint32_t *>(table);
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint32_t i = (uint32_t)s * kPer + k;
+            const uint32_t e1 = entry(i), l1 = e1 & 0xFF;
+            const uint32_t e2 = entry((i << l1) & (kLutEntries - 1)), l2 = e2 & 0xFF;
+            const bool both = l1 + l2 <= kMaxLen;
+            plut[i] = (both ? l1 + l2 : l1) | (e1 & 0xFF00u) | (both ? (e2 & 0xFF00u) << 8 : 0u) | (l1 << 24) |
+                      (both ? kPairBit : 0u);
+        }
+        return;
+    }
+    uint16_t *lut = static_cast<uint16_t *>(table);
     // a code of <= 10 bits owns whole 4-aligned blocks of the index space
     auto fill4 = [&](uint32_t i0) {
         const uint32_t e0 = entry(i0);
@@ -233,7 +253,7 @@ __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t 
     sb = sym_pair(b1, b2);
 }
 
-// A second table over the same 12-bit windows, built from the first. Entry
+// A second table over the same 12-bit windows (build_lut<.., true>). Entry
 // i (32 bits) describes the codes that start window i:
 //   byte 0   bits to consume: both codes' lengths when the second code also
 //            ends inside the window, else the first code's length;
@@ -245,25 +265,6 @@ __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t 
 // two dependent ones. The restore and the matrix-vector kernel decode
 // through it: the restore's first and last chunks, and all of the fused
 // kernel's, are bound by the decode.
-constexpr uint32_t kPairBit = 0x80000000u;
-
-// Fill the pair table from the one-code table (both in LDS); all kNThreads
-// threads take part, and callers bracket it with barriers.
-template <int kNThreads = kThreads>
-__device__ void build_pair_lut(const uint16_t *lut, uint32_t *plut) {
-    constexpr uint32_t kPer = kLutEntries / kNThreads;
-    static_assert(kLutEntries % kNThreads == 0, "whole entries per thread");
-#pragma unroll
-    for (uint32_t k = 0; k < kPer; ++k) {
-        const uint32_t i = (uint32_t)threadIdx.x * kPer + k;
-        const uint32_t e1 = lut[i], l1 = e1 & 0xFF;
-        const uint32_t e2 = lut[(i << l1) & (kLutEntries - 1)], l2 = e2 & 0xFF;
-        const bool both = l1 + l2 <= kMaxLen;
-        plut[i] = (both ? l1 + l2 : l1) | (e1 & 0xFF00u) | (both ? (e2 & 0xFF00u) << 8 : 0u) | (l1 << 24) |
-                  (both ? kPairBit : 0u);
-    }
-}
-
 // A pair entry whose window holds only one whole code, completed by the
 // entry e2 of the window shifted past that code.
 __device__ inline uint32_t complete_entry(uint32_t e, uint32_t e2) {

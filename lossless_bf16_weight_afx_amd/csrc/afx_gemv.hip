@@ -267,9 +267,7 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
 
 // The workgroup's LDS as one object, the decode table first: at LDS address
 // 0 a table read needs no base added to its index (the base of a table
-// placed higher does not fit the read instruction's 16-bit offset). The
-// one-code table is built in the staging area and turned into the pair
-// table before any chunk is staged.
+// placed higher does not fit the read instruction's 16-bit offset).
 struct GemvLds {
     uint32_t plut[kLutEntries];                   // 16 KB
     uint32_t stage[kWavesPerBlock][kStageRow];    // 98 KB
@@ -288,8 +286,6 @@ void afx_gemv_kernel(const GemvBatch batch) {
     __shared__ __attribute__((aligned(16))) GemvLds lds;
     uint32_t *plut = lds.plut;
     auto &stage = lds.stage;
-    uint16_t *lut = reinterpret_cast<uint16_t *>(&lds.stage[0][0]);  // the one-code table, while building
-    static_assert(sizeof(lds.stage) >= kLutEntries * sizeof(uint16_t), "room for the one-code table");
     LutScratch &scratch = lds.scratch;
     uint32_t &next_j = lds.next_j;
     uint16_t *xs = lds.xs;
@@ -337,10 +333,8 @@ void afx_gemv_kernel(const GemvBatch batch) {
         if (x_in_lds)
             for (uint32_t i = threadIdx.x; i < xbytes / 16; i += kThreads)
                 reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(a.x)[i];
-        build_lut(wave < kSymbolWaves ? len_any : 0u, lut, scratch);
-        __syncthreads();
-        build_pair_lut(lut, plut);
-        __syncthreads();  // the pair table is complete and the staging area free
+        build_lut<kThreads, true>(wave < kSymbolWaves ? len_any : 0u, plut, scratch);
+        __syncthreads();  // the pair table is complete
         if (!has_c) continue;
         uint2 smv[8];
         load_signmant(T, k + (uint64_t)jc * nb, lane, smv);
