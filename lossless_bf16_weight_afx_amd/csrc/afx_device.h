@@ -238,9 +238,9 @@ __device__ inline void buf_advance(BufChain &c, const uint32_t *stage, uint32_t 
 }
 
 // Two symbols per chain through the one-code table, two dependent table
-// reads per step; sa, sb: the symbols as bytes 0, 1. (The MFMA product,
-// which builds its table once per 64-row tile, measured 7-8% slower with the
-// pair table below.)
+// reads per step; sa, sb: the symbols as bytes 0, 1. (The MFMA product, with
+// two waves per SIMD, measured about 5% slower with the pair table below,
+// also when that table was built as cheaply as the one-code table.)
 __device__ inline void buf_chain_pairs(BufChain &a, BufChain &b, const uint32_t *stage, const uint16_t *lut,
                                        uint32_t &sa, uint32_t &sb) {
     const uint32_t wa = __builtin_amdgcn_alignbit(a.hi, a.lo, a.r);
