@@ -357,3 +357,38 @@ def test_graph_replays_bit_exact():
         torch.cuda.synchronize()
         for o, r in zip(outs, refs):
             assert torch.equal(o, r), f"replay {rep}"
+
+
+def test_two_streams_at_once():
+    """Two batches restored at the same time on two streams (default
+    priority): the library keeps no state between or during calls, so the
+    launches may overlap; both come out bit-exact, three times over."""
+    T = synth.TensorSpec
+    sets = [[T(f"c{k}a", (1024, 2048), "normal", 950 + k), T(f"c{k}b", (300, 5120), "t4", 960 + k),
+             T(f"c{k}c", (5000,), "normal", 970 + k)] for k in range(2)]
+    jobsets, outsets, refsets, keep = [], [], [], []
+    for specs in sets:
+        xs = [synth.generate(sp) for sp in specs]
+        blobs = [oracle.encode(x, sp.shape) for x, sp in zip(xs, specs)]
+        infos = [afx.afx_query(b) for b in blobs]
+        dblobs = [afx.to_device(b) for b in blobs]
+        outs = [torch.zeros(x.size, dtype=torch.int16, device="cuda") for x in xs]
+        jobsets.append(afx.make_jobs([(i, db.data_ptr(), o.data_ptr(), 2 * x.size)
+                                      for i, db, o, x in zip(infos, dblobs, outs, xs)]))
+        outsets.append(outs)
+        refsets.append([torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs])
+        keep.append((infos, dblobs))
+    say("[gpu] case two batches restored concurrently on two streams")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for outs in outsets:
+            for o in outs:
+                o.fill_(0x2345 + rep)
+        torch.cuda.synchronize()
+        for jobs, st in zip(jobsets, streams):
+            with torch.cuda.stream(st):
+                afx.afx_decode_layer_async(jobs, st.cuda_stream)
+        torch.cuda.synchronize()
+        for outs, refs in zip(outsets, refsets):
+            for o, r in zip(outs, refs):
+                assert torch.equal(o, r), f"pass {rep}"

@@ -130,3 +130,38 @@ def test_batch_of_long_rows(m):
     for (info, db, xd, y), (ref, bound), shape in zip(keep, refs, shapes):
         err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
         assert np.all(err <= bound), shape
+
+
+def test_graph_replays_within_bound():
+    """A fused matrix-vector product captured in a HIP graph (through
+    torch.cuda.graph) after a fill kernel that clears y, replayed three
+    times with eager work in between; every replay within its bound."""
+    rows, cols, m = 200, 4096, 2
+    w = synth.generate(synth.TensorSpec("gw", (rows, cols), "normal", 4242))
+    blob = oracle.encode(w, (rows, cols))
+    info = afx.afx_query(blob)
+    db = afx.to_device(blob)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(43).standard_normal((m, cols)).astype(np.float32))
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+    ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4)
+    say("[gpu] case graph capture of a fused matrix-vector product")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        y.zero_()
+        afx.afx_restore_gemv_async(info, db.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(), side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y.zero_()  # a fill kernel, not a memset node
+        afx.afx_restore_gemv_async(info, db.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        y.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound), f"replay {rep}"
