@@ -174,3 +174,38 @@ def test_batches_over_sixteen_matrices():
             ref, bound = oracle.restore_gemv(blob, rows, cols, x)
             err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
             assert np.all(err <= tol * bound), (name, rows, cols)
+
+
+def test_graph_replays_exact():
+    """The MFMA product captured in a HIP graph (through torch.cuda.graph)
+    after a fill kernel that clears y, replayed three times with eager work
+    in between; on integer data every replay equals the oracle exactly."""
+    rows, cols, m = 128, 2816, 40
+    rng = np.random.default_rng(77)
+    w = small_ints(rng, rows * cols, -3, 3)
+    x = small_ints(rng, (m, cols), -2, 2)
+    blob = oracle.encode(w, (rows, cols))
+    info = afx.afx_query(blob)
+    db = afx.to_device(blob)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+    ref, _ = oracle.restore_gemv(blob, rows, cols, x, threads=4)
+    say("[gpu] case graph capture of an MFMA product")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        y.zero_()
+        afx.afx_restore_gemm_async(info, db.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(), side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y.zero_()  # a fill kernel, not a memset node
+        afx.afx_restore_gemm_async(info, db.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        y.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), ref), f"replay {rep}"
