@@ -138,7 +138,13 @@ int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len
 
 /* afx_encode: write the blob for x with the lengths and stream length from
  * afx_encode_plan into blob (host memory, blob_bytes >= the planned size).
- * shape has ndim entries (ndim 1..4, product == n). */
+ * shape has ndim entries (ndim 1..4, product == n). Errors: AFX_E_INVALID_ARG
+ * (NULL pointer, ndim out of range, shape product != n, code_len not a
+ * complete prefix code of lengths <= 12 -- Kraft sum 1, or one symbol of
+ * length 1 --, an exponent of x without a code, total_bits not the stream
+ * length those lengths give x), AFX_E_UNSUPPORTED (n above 2^40),
+ * AFX_E_BUFFER_TOO_SMALL (blob_bytes below the blob size). On an error the
+ * blob's contents are unspecified. */
 int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape,
                const uint8_t code_len[256], uint64_t total_bits, void *blob, size_t blob_bytes,
                int threads);

@@ -214,7 +214,8 @@ def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None, plan=None)
     if out is None:
         out = np.empty(nbytes, np.uint8)
     if isinstance(out, np.ndarray):
-        assert out.dtype == np.uint8 and out.size >= nbytes
+        if out.dtype != np.uint8 or not out.flags.c_contiguous:
+            raise ValueError("out must be a contiguous uint8 array")
         addr, cap = out.ctypes.data, out.size
     else:
         addr, cap = int(out[0]), int(out[1])

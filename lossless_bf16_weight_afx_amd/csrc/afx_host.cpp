@@ -323,15 +323,29 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
     if ((!x && n) || !code_len || !blob_out || ndim < 1 || ndim > 4 || !shape) return AFX_E_INVALID_ARG;
     if (n > kMaxElems) return AFX_E_UNSUPPORTED;
     uint64_t prod = 1;
-    for (uint32_t d = 0; d < ndim; ++d) prod *= shape[d];
+    for (uint32_t d = 0; d < ndim; ++d) {
+        if (shape[d] && prod > kMaxElems / shape[d]) return AFX_E_INVALID_ARG;  // would wrap
+        prod *= shape[d];
+    }
     if (prod != n) return AFX_E_INVALID_ARG;
-    const Layout L = layout_for(n, total_bits);
-    if (blob_bytes < L.blob_bytes) return AFX_E_BUFFER_TOO_SMALL;
-    uint32_t used = 0;
+    if (total_bits > n * kMaxLen) return AFX_E_INVALID_ARG;
+    // The lengths must form a complete prefix code (as afx_query demands):
+    // Kraft sum exactly 1, or a single symbol of length 1.
+    uint32_t used = 0, longest = 0;
+    uint64_t kraft = 0;  // in units of 2^-12
     for (int s = 0; s < 256; ++s) {
         if (code_len[s] > kMaxLen) return AFX_E_INVALID_ARG;
-        used += code_len[s] != 0;
+        if (code_len[s]) {
+            ++used;
+            longest = std::max<uint32_t>(longest, code_len[s]);
+            kraft += (uint64_t)1 << (kMaxLen - code_len[s]);
+        }
     }
+    if ((n == 0) != (used == 0)) return AFX_E_INVALID_ARG;
+    if (used == 1 && longest != 1) return AFX_E_INVALID_ARG;
+    if (used >= 2 && kraft != ((uint64_t)1 << kMaxLen)) return AFX_E_INVALID_ARG;
+    const Layout L = layout_for(n, total_bits);
+    if (blob_bytes < L.blob_bytes) return AFX_E_BUFFER_TOO_SMALL;
     uint32_t code[256];
     canonical(code_len, code);
     uint8_t *b = static_cast<uint8_t *>(blob_out);

@@ -164,3 +164,40 @@ def test_encoder_lengths_match_oracle_optimum_on_random_histograms():
         lo = oracle.sections(oracle.encode(x))["header"]["total_bits"]
         hi = oracle.sections(afx.afx_encode(x))["header"]["total_bits"]
         assert lo == hi
+
+
+def test_encoder_rejects_bad_plans():
+    """afx_encode refuses lengths that are not a complete prefix code, a
+    shape whose product is not n (also when the product wraps), a wrong
+    stream length and a buffer below the blob size; every refusal is an
+    error status, never a blob that afx_query would reject."""
+    rng = np.random.default_rng(8)
+    x = rng.integers(0, 1 << 16, size=5000, dtype=np.uint16)
+    lens, bits, nbytes = afx.afx_encode_plan(x)
+
+    def status(lens=lens, bits=bits, shape=(5000,), cap=nbytes):
+        with pytest.raises(afx.AfxError) as e:
+            afx.afx_encode(x, shape, out=np.empty(cap, np.uint8), plan=(lens, bits, nbytes))
+        return e.value.status
+
+    short = lens.copy()
+    short[np.flatnonzero(short)[0]] += 1  # Kraft sum below 1: not complete
+    assert status(lens=short) == afx.AFX_E_INVALID_ARG
+    over = lens.copy()
+    k = np.flatnonzero(over == over.max())[0]
+    over[k] -= 1  # Kraft sum above 1: not a prefix code
+    assert status(lens=over) == afx.AFX_E_INVALID_ARG
+    missing = lens.copy()
+    missing[(int(x[0]) >> 7) & 0xFF] = 0  # an exponent of x without a code
+    assert status(lens=missing) == afx.AFX_E_INVALID_ARG
+    assert status(bits=bits + 1) == afx.AFX_E_INVALID_ARG
+    assert status(shape=(50, 101)) == afx.AFX_E_INVALID_ARG
+    assert status(shape=((1 << 62) + 1250, 4)) == afx.AFX_E_INVALID_ARG  # 2^64 + 5000 wraps to 5000
+    assert status(cap=nbytes - 1) == afx.AFX_E_BUFFER_TOO_SMALL
+    one = np.zeros(256, np.uint8)
+    one[3] = 2  # a single symbol must take length 1
+    y = np.full(10, 3 << 7, np.uint16)
+    with pytest.raises(afx.AfxError) as e:
+        afx.afx_encode(y, plan=(one, 20, 1 << 12))
+    assert e.value.status == afx.AFX_E_INVALID_ARG
+    assert np.array_equal(oracle.decode(afx.afx_encode(x, (50, 100))), x)  # the plan itself is fine
