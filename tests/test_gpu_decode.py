@@ -194,6 +194,43 @@ def test_embedding_full_size():
     assert torch.equal(out, xd)
 
 
+def test_more_than_2_32_values():
+    """A tensor of 2^32 + 3 * 4096 + 77 values: element indices, sign/mantissa
+    byte offsets and output byte offsets all pass 2^32, and the last chunk is
+    ragged. The values repeat with a period of 2^24 + 4099, which shares no
+    factor with the chunk size, so no two chunks hold the same values. The
+    blob comes from the library's encoder (the oracle's bit-serial encoder
+    takes minutes at this size); the oracle decoder checks it on the chunks
+    at the start, around element 2^32 and at the end. The GPU restore must
+    equal the input in full."""
+    n = (1 << 32) + 3 * 4096 + 77
+    period = (1 << 24) + 4099
+    say("[gpu] generate 2^32+ values")
+    rng = np.random.default_rng(42)
+    base = (rng.standard_normal(period, dtype=np.float32) * 0.02).view(np.uint32)
+    base = (base >> 16).astype(np.uint16)  # BF16 bits, truncated
+    x = np.empty(n, np.uint16)
+    for o in range(0, n, period):
+        k = min(period, n - o)
+        x[o:o + k] = base[:k]
+    say("[gpu] encode 2^32+ values")
+    blob = afx.afx_encode(x, (n,))
+    info = afx.afx_query(blob)
+    assert int(info.n_elems) == n
+    c_mid, c_hi = (1 << 32) // 4096, int(info.n_chunks)
+    for c0, c1 in ((0, 3), (c_mid - 2, c_mid + 2), (c_hi - 2, c_hi)):
+        assert np.array_equal(oracle.decode_chunks(blob, c0, c1), x[c0 * 4096:min(c1 * 4096, n)])
+    dev = afx.to_device(blob)
+    del blob
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    del x
+    out = torch.full((n + 64,), 0x5A5A, dtype=torch.int16, device="cuda")
+    say(f"[gpu] case n={n}")
+    afx.afx_decode_tensor(info, dev.data_ptr(), out.data_ptr(), 2 * n, torch.cuda.current_stream().cuda_stream)
+    assert torch.equal(out[:n], xd)
+    assert bool((out[n:] == 0x5A5A).all()), "wrote past the output"
+
+
 def test_streamed_units_double_buffered():
     """Units copied from pinned host memory on a side stream while the
     previous unit is restored; every unit bit-exact."""
