@@ -209,3 +209,56 @@ def test_graph_replays_exact():
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().astype(np.float64), ref), f"replay {rep}"
+
+
+def test_fused_products_past_2_32_weights():
+    """One matrix of 1,048,640 x 4096 weights (more than 2^32): element
+    offsets, sign/mantissa byte offsets and row indices pass 32 bits. The
+    integer weights repeat with a period of 2^24 + 4099, prime to the chunk
+    size and the row length. Both fused products, the matrix-vector one
+    (m = 1) and the MFMA one (m = 8), must equal y = W x exactly (integer
+    sums below 2^24 are exact in FP32). The blob comes from the library's
+    encoder; the oracle decoder checks it on chunks at the start, around
+    element 2^32 and at the end."""
+    rows, cols = 1_048_640, 4096
+    n = rows * cols
+    period = (1 << 24) + 4099
+    rng = np.random.default_rng(99)
+    vals = rng.integers(-3, 4, size=period).astype(np.int8)
+    pat = synth.f32_to_bf16_bits(vals.astype(np.float32))
+    say("[gpu] generate 2^32+ integer weights")
+    w = np.empty(n, np.uint16)
+    for o in range(0, n, period):
+        k = min(period, n - o)
+        w[o:o + k] = pat[:k]
+    say("[gpu] encode 2^32+ weights")
+    blob = afx.afx_encode(w, (rows, cols))
+    info = afx.afx_query(blob)
+    c_mid, c_hi = (1 << 32) // 4096, int(info.n_chunks)
+    for c0, c1 in ((0, 3), (c_mid - 2, c_mid + 2), (c_hi - 2, c_hi)):
+        assert np.array_equal(oracle.decode_chunks(blob, c0, c1), w[c0 * 4096:min(c1 * 4096, n)])
+    del w
+    dev = afx.to_device(blob)
+    del blob
+    x8 = rng.integers(-2, 3, size=(8, cols)).astype(np.float32)
+    say("[gpu] reference y = W x in blocks of rows")
+    ref = np.empty((8, rows), np.float32)
+    blk = 1 << 16  # rows per block; a block's weights are a slice of the repeated pattern
+    reps = np.tile(vals, (blk * cols) // period + 2)
+    for r0 in range(0, rows, blk):
+        nr = min(blk, rows - r0)
+        o = (r0 * cols) % period
+        wb = reps[o:o + nr * cols].reshape(nr, cols).astype(np.float32)
+        ref[:, r0:r0 + nr] = (wb @ x8.T).T
+    del reps, wb
+    xd = torch.from_numpy(synth.f32_to_bf16_bits(x8).view(np.int16)).to("cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for m, name in ((1, "matrix-vector"), (8, "MFMA")):
+        y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+        say(f"[gpu] case {name} product, {rows}x{cols}, m={m}")
+        if m == 1:
+            afx.afx_restore_gemv_async(info, dev.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(), stream)
+        else:
+            afx.afx_restore_gemm_async(info, dev.data_ptr(), rows, cols, xd.data_ptr(), m, y.data_ptr(), stream)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), ref[:m]), name
