@@ -136,6 +136,18 @@ def status_str(status: int) -> str:
     return lib().afx_status_str(status).decode()
 
 
+def _host_bytes(a: np.ndarray, nbytes: int | None) -> tuple[int, int]:
+    """Address and size of a blob held in a numpy array; a size given with
+    the array may not exceed it (the library would read past its end)."""
+    if a.dtype != np.uint8 or not a.flags.c_contiguous:
+        raise ValueError("a blob must be a contiguous uint8 array")
+    if nbytes is None:
+        return a.ctypes.data, a.size
+    if not 0 <= int(nbytes) <= a.size:
+        raise ValueError(f"blob size {nbytes} outside the array's {a.size} bytes")
+    return a.ctypes.data, int(nbytes)
+
+
 def _check(rc: int, what: str) -> None:
     if rc != AFX_OK:
         raise AfxError(rc, what)
@@ -148,8 +160,7 @@ def afx_query(blob_host, blob_bytes: int | None = None) -> afx_info:
     """Validate a host blob (numpy uint8 array, or an address with a size)."""
     info = afx_info()
     if isinstance(blob_host, np.ndarray):
-        assert blob_host.dtype == np.uint8 and blob_host.flags.c_contiguous
-        ptr, size = blob_host.ctypes.data, blob_host.size if blob_bytes is None else blob_bytes
+        ptr, size = _host_bytes(blob_host, blob_bytes)
     else:
         ptr, size = int(blob_host), int(blob_bytes)
     _check(lib().afx_query(ctypes.c_void_p(ptr), size, ctypes.byref(info)), "afx_query")
@@ -275,14 +286,14 @@ def afx_decode_host(blob, blob_bytes: int | None = None, out=None, threads: int 
     a numpy uint16 array, an (address, capacity) pair, or None (allocated).
     Returns the uint16 array, or None when out is an address pair."""
     if isinstance(blob, np.ndarray):
-        assert blob.dtype == np.uint8 and blob.flags.c_contiguous
-        addr, size = blob.ctypes.data, blob.size if blob_bytes is None else blob_bytes
+        addr, size = _host_bytes(blob, blob_bytes)
     else:
         addr, size = int(blob), int(blob_bytes)
     if out is None:
         out = np.empty(int(afx_query(addr, size).n_elems), np.uint16)
     if isinstance(out, np.ndarray):
-        assert out.dtype == np.uint16 and out.flags.c_contiguous
+        if out.dtype != np.uint16 or not out.flags.c_contiguous:
+            raise ValueError("out must be a contiguous uint16 array")
         oaddr, cap = out.ctypes.data, 2 * out.size
     else:
         oaddr, cap = int(out[0]), int(out[1])

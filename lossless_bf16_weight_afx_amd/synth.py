@@ -122,7 +122,8 @@ def generate(spec: TensorSpec, out: np.ndarray | None = None, threads: int | Non
     n = spec.numel
     if out is None:
         out = np.empty(n, np.uint16)
-    assert out.dtype == np.uint16 and out.size == n
+    if out.dtype != np.uint16 or out.size != n or not out.flags.c_contiguous:
+        raise ValueError(f"out must be a contiguous uint16 array of {n} values")
     nb = block_count(n)
     if threads is None:
         threads = min(16, os.cpu_count() or 1)

@@ -201,3 +201,18 @@ def test_encoder_rejects_bad_plans():
         afx.afx_encode(y, plan=(one, 20, 1 << 12))
     assert e.value.status == afx.AFX_E_INVALID_ARG
     assert np.array_equal(oracle.decode(afx.afx_encode(x, (50, 100))), x)  # the plan itself is fine
+
+
+def test_binding_refuses_sizes_past_the_array():
+    """A size given with a numpy blob may not exceed the array: the library
+    would read past its end. Wrong dtypes are refused too."""
+    x, blob = c1_blob()
+    with pytest.raises(ValueError):
+        afx.afx_query(blob, blob.size + 1)
+    with pytest.raises(ValueError):
+        afx.afx_query(blob.view(np.int8))
+    with pytest.raises(ValueError):
+        afx.afx_decode_host(blob, blob.size + 64)
+    with pytest.raises(ValueError):
+        afx.afx_decode_host(blob, out=np.empty(x.size, np.int16))
+    assert afx.afx_query(blob, blob.size).n_elems == x.size
