@@ -148,6 +148,15 @@ def _host_bytes(a: np.ndarray, nbytes: int | None) -> tuple[int, int]:
     return a.ctypes.data, int(nbytes)
 
 
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns as a contiguous uint16 array. Only 16-bit integer
+    arrays hold them; a cast from any other type would change the bits."""
+    x = np.asarray(x)
+    if x.dtype not in (np.uint16, np.int16):
+        raise TypeError(f"BF16 bit patterns must be uint16 or int16, not {x.dtype}")
+    return np.ascontiguousarray(x).view(np.uint16)
+
+
 def _check(rc: int, what: str) -> None:
     if rc != AFX_OK:
         raise AfxError(rc, what)
@@ -198,7 +207,7 @@ def afx_decode_layer_async(jobs, stream: int = 0) -> None:
 
 def afx_encode_plan(x: np.ndarray, threads: int = 0):
     """Code lengths (256 u8), stream bits and blob size for BF16 bits x."""
-    x = np.ascontiguousarray(x, dtype=np.uint16).ravel()
+    x = _bf16_bits(x).ravel()
     lens = np.zeros(256, np.uint8)
     bits = ctypes.c_uint64()
     nbytes = ctypes.c_uint64()
@@ -216,7 +225,7 @@ def afx_encode(x: np.ndarray, shape=None, threads: int = 0, out=None, plan=None)
     are returned as a numpy view when out is an array or None, else the size
     is returned. ``plan`` is a result of afx_encode_plan for the same x.
     """
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+    x = _bf16_bits(x)
     if shape is None:
         shape = x.shape if x.ndim else (1,)
     x = x.ravel()

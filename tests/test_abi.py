@@ -216,3 +216,14 @@ def test_binding_refuses_sizes_past_the_array():
     with pytest.raises(ValueError):
         afx.afx_decode_host(blob, out=np.empty(x.size, np.int16))
     assert afx.afx_query(blob, blob.size).n_elems == x.size
+
+
+def test_encoder_takes_only_16_bit_patterns():
+    """The encoder's input is BF16 bit patterns: uint16 or int16 (same bits);
+    any other type is refused rather than cast."""
+    x = synth.generate(synth.TensorSpec("t", (5000,), "normal", 4))
+    assert np.array_equal(afx.afx_encode(x.view(np.int16)), afx.afx_encode(x))
+    with pytest.raises(TypeError):
+        afx.afx_encode(x.astype(np.float32))
+    with pytest.raises(TypeError):
+        afx.afx_encode_plan(x.astype(np.int32))
