@@ -60,8 +60,13 @@ typedef enum afx_status {
     AFX_E_MISALIGNED = -6,      /* device pointer not 16-byte aligned */
     AFX_E_HIP = -7,             /* a HIP runtime call failed (launch or execution) */
     AFX_E_UNSUPPORTED = -8,     /* request beyond what this build supports */
-    AFX_E_IO = -9               /* a file could not be opened or read in full */
+    AFX_E_IO = -9,              /* a file could not be opened or read in full */
+    AFX_E_HOST_MEMORY = -10     /* host memory for the call's own work could not be had */
 } afx_status;
+/* No entry point throws, aborts or prints: the host-side calls that allocate
+ * working memory (the encoder, the host unpack, the file reader) return
+ * AFX_E_HOST_MEMORY when it cannot be had, and run on fewer threads when
+ * threads cannot be started. */
 
 /* What afx_query reports about a blob. Offsets are in bytes from the blob's
  * first byte; sizes count elements unless named *_bytes. */

@@ -23,6 +23,7 @@ AFX_E_MISALIGNED = -6
 AFX_E_HIP = -7
 AFX_E_UNSUPPORTED = -8
 AFX_E_IO = -9
+AFX_E_HOST_MEMORY = -10
 MAX_JOBS_PER_LAUNCH = 32
 AFX_READ_DIRECT = 1
 

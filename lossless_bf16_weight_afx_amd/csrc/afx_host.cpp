@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <new>
 #include <thread>
 #include <vector>
 
@@ -48,14 +49,9 @@ void parallel_ranges(int threads, uint64_t items, F &&fn) {
         fn(0, (uint64_t)0, items);
         return;
     }
-    std::vector<std::thread> pool;
-    pool.reserve(threads);
-    for (int t = 0; t < threads; ++t) {
-        uint64_t a = items * (uint64_t)t / (uint64_t)threads;
-        uint64_t b = items * (uint64_t)(t + 1) / (uint64_t)threads;
-        pool.emplace_back([&fn, t, a, b] { fn(t, a, b); });
-    }
-    for (auto &th : pool) th.join();
+    run_parts(threads, [&](int t) {
+        fn(t, items * (uint64_t)t / (uint64_t)threads, items * (uint64_t)(t + 1) / (uint64_t)threads);
+    });
 }
 
 }  // namespace
@@ -290,12 +286,13 @@ const char *afx_status_str(int status) {
         case AFX_E_HIP: return "HIP runtime error";
         case AFX_E_UNSUPPORTED: return "unsupported request";
         case AFX_E_IO: return "file could not be opened or read in full";
+        case AFX_E_HOST_MEMORY: return "host memory could not be allocated";
         default: return "unknown status";
     }
 }
 
-int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len[256], uint64_t *total_bits,
-                    uint64_t *blob_bytes) {
+static int encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len[256], uint64_t *total_bits,
+                       uint64_t *blob_bytes) {
     if ((!x && n) || !code_len || !total_bits || !blob_bytes) return AFX_E_INVALID_ARG;
     if (n > kMaxElems) return AFX_E_UNSUPPORTED;
     const int T = thread_count(threads, n / (1 << 20) + 1);
@@ -318,8 +315,8 @@ int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len
     return AFX_OK;
 }
 
-int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape, const uint8_t code_len[256],
-               uint64_t total_bits, void *blob_out, size_t blob_bytes, int threads) {
+static int encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape, const uint8_t code_len[256],
+                  uint64_t total_bits, void *blob_out, size_t blob_bytes, int threads) {
     if ((!x && n) || !code_len || !blob_out || ndim < 1 || ndim > 4 || !shape) return AFX_E_INVALID_ARG;
     if (n > kMaxElems) return AFX_E_UNSUPPORTED;
     uint64_t prod = 1;
@@ -450,6 +447,24 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
     for (auto &e : edges)
         if (e.word != ~(uint64_t)0) words[e.word] |= e.bits;
     return AFX_OK;
+}
+
+int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len[256], uint64_t *total_bits,
+                    uint64_t *blob_bytes) {
+    try {
+        return encode_plan(x, n, threads, code_len, total_bits, blob_bytes);
+    } catch (const std::bad_alloc &) {
+        return AFX_E_HOST_MEMORY;
+    }
+}
+
+int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape, const uint8_t code_len[256],
+               uint64_t total_bits, void *blob_out, size_t blob_bytes, int threads) {
+    try {
+        return encode(x, n, ndim, shape, code_len, total_bits, blob_out, blob_bytes, threads);
+    } catch (const std::bad_alloc &) {
+        return AFX_E_HOST_MEMORY;
+    }
 }
 
 }  // extern "C"

@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <new>
 #include <thread>
 #include <vector>
 
@@ -99,7 +100,7 @@ void decode_chunk(const Tensor &T, uint64_t c, uint16_t *out) {
 
 }  // namespace
 
-extern "C" int afx_decode_host(const void *blob, size_t blob_bytes, uint16_t *out, size_t out_bytes, int threads) {
+static int decode_host(const void *blob, size_t blob_bytes, uint16_t *out, size_t out_bytes, int threads) {
     if (!blob) return AFX_E_INVALID_ARG;
     afx_info info;
     int rc = afx_query(blob, blob_bytes, &info);
@@ -124,13 +125,14 @@ extern "C" int afx_decode_host(const void *blob, size_t blob_bytes, uint16_t *ou
     auto work = [&](uint64_t c0, uint64_t c1) {
         for (uint64_t c = c0; c < c1; ++c) decode_chunk(T, c, out);
     };
-    if (t == 1) {
-        work(0, chunks);
-    } else {
-        std::vector<std::thread> pool;
-        pool.reserve(t);
-        for (int i = 0; i < t; ++i) pool.emplace_back(work, chunks * i / t, chunks * (i + 1) / t);
-        for (auto &th : pool) th.join();
-    }
+    afx::run_parts(t, [&](int i) { work(chunks * i / t, chunks * (i + 1) / t); });
     return AFX_OK;
+}
+
+extern "C" int afx_decode_host(const void *blob, size_t blob_bytes, uint16_t *out, size_t out_bytes, int threads) {
+    try {
+        return decode_host(blob, blob_bytes, out, out_bytes, threads);
+    } catch (const std::bad_alloc &) {
+        return AFX_E_HOST_MEMORY;
+    }
 }

@@ -4,6 +4,8 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <thread>
+#include <vector>
 
 #include "../../include/afx.h"
 
@@ -28,6 +30,26 @@ int limited_lengths(const uint64_t freq[256], int limit, uint8_t len[256]);
 void canonical(const uint8_t len[256], uint32_t code[256]);
 int validate(const uint8_t *blob, size_t nbytes, afx_info *out);
 int check_info(const afx_info *info);
+
+// Run fn(i) for every part i in [0, t), one thread per part; the calling
+// thread takes part 0, and also every part whose thread could not be started
+// (so all parts run, and nothing here throws). fn must not throw.
+template <class F>
+void run_parts(int t, F &&fn) noexcept {
+    std::vector<std::thread> pool;
+    int started = 1;
+    try {
+        pool.reserve(t > 1 ? (size_t)(t - 1) : 0);
+        for (; started < t; ++started) {
+            const int i = started;
+            pool.emplace_back([&fn, i] { fn(i); });
+        }
+    } catch (...) {
+    }
+    fn(0);
+    for (int i = started; i < t; ++i) fn(i);
+    for (auto &th : pool) th.join();
+}
 
 // Whether byte ranges [a, a + an) and [b, b + bn) share a byte.
 inline bool ranges_overlap(const void *a, uint64_t an, const void *b, uint64_t bn) {

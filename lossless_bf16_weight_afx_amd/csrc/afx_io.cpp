@@ -52,6 +52,7 @@ extern "C" int afx_file_read(const char *path, uint64_t offset, uint64_t bytes, 
                              unsigned flags) {
     if (!path || (!dst && bytes) || (flags & ~AFX_READ_DIRECT)) return AFX_E_INVALID_ARG;
     if (bytes == 0) return AFX_OK;
+    if (offset > (uint64_t)INT64_MAX || bytes > (uint64_t)INT64_MAX - offset) return AFX_E_INVALID_ARG;
     const bool direct = flags & AFX_READ_DIRECT;
     const int fd = open(path, O_RDONLY | O_CLOEXEC | (direct ? O_DIRECT : 0));
     if (fd < 0) return direct && errno == EINVAL ? AFX_E_UNSUPPORTED : AFX_E_IO;
@@ -65,12 +66,20 @@ extern "C" int afx_file_read(const char *path, uint64_t offset, uint64_t bytes, 
     if ((uint64_t)t > pieces) t = (int)pieces;
     std::atomic<uint64_t> next{0};
     std::atomic<bool> ok{true};
-    auto worker = [&] {
+    std::atomic<int> status{AFX_OK};
+    auto fail = [&](int rc) {
+        int expected = AFX_OK;
+        status.compare_exchange_strong(expected, rc);
+        ok = false;
+    };
+    // Workers take pieces from one counter until none is left, so any
+    // number of them reads the whole range.
+    auto worker = [&](int) {
         uint8_t *bounce = nullptr;
         if (direct) {
             bounce = static_cast<uint8_t *>(std::aligned_alloc(kDirectAlign, kPiece));
             if (!bounce) {
-                ok = false;
+                fail(AFX_E_HOST_MEMORY);
                 return;
             }
         }
@@ -78,13 +87,14 @@ extern "C" int afx_file_read(const char *path, uint64_t offset, uint64_t bytes, 
             const uint64_t at = lo + p * kPiece;              // file offset of this piece
             const uint64_t want = std::min(kPiece, end - at);  // bytes of it inside [lo, end)
             if (!direct) {
-                if (read_upto(fd, static_cast<uint8_t *>(dst) + (at - offset), want, at) != (int64_t)want) ok = false;
+                if (read_upto(fd, static_cast<uint8_t *>(dst) + (at - offset), want, at) != (int64_t)want)
+                    fail(AFX_E_IO);
                 continue;
             }
             const uint64_t len = (want + kDirectAlign - 1) / kDirectAlign * kDirectAlign;
             const int64_t got = read_upto(fd, bounce, len, at);
             if (got < (int64_t)want) {
-                ok = false;
+                fail(AFX_E_IO);
                 continue;
             }
             const uint64_t from = std::max(at, offset);  // the part of the piece the caller asked for
@@ -92,14 +102,7 @@ extern "C" int afx_file_read(const char *path, uint64_t offset, uint64_t bytes, 
         }
         std::free(bounce);
     };
-    if (t == 1) {
-        worker();
-    } else {
-        std::vector<std::thread> pool;
-        pool.reserve(t);
-        for (int i = 0; i < t; ++i) pool.emplace_back(worker);
-        for (auto &th : pool) th.join();
-    }
+    afx::run_parts(t, worker);
     close(fd);
-    return ok ? AFX_OK : AFX_E_IO;
+    return status.load();
 }

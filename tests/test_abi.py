@@ -227,3 +227,18 @@ def test_encoder_takes_only_16_bit_patterns():
         afx.afx_encode(x.astype(np.float32))
     with pytest.raises(TypeError):
         afx.afx_encode_plan(x.astype(np.int32))
+
+
+def test_every_status_has_its_own_text(tmp_path):
+    codes = [v for k, v in vars(afx).items() if k.startswith("AFX_E_")]
+    assert afx.AFX_E_HOST_MEMORY in codes
+    texts = [afx.status_str(c) for c in codes]
+    assert "unknown status" not in texts and len(set(texts)) == len(codes)
+    # a byte range whose end does not fit a file offset is refused before any read
+    p = tmp_path / "f.bin"
+    p.write_bytes(b"x" * 64)
+    dst = np.empty(16, np.uint8)
+    for off, n in (((1 << 63) - 8, 16), (1 << 63, 1), (8, (1 << 64) - 4)):
+        with pytest.raises(afx.AfxError) as e:
+            afx.afx_file_read(str(p), off, n, dst.ctypes.data, direct=False)
+        assert e.value.status == afx.AFX_E_INVALID_ARG
