@@ -1,7 +1,11 @@
 """GPU parity: the HIP restore against the original bits and the CPU oracle.
 
-Blobs come from the oracle's encoder; the expected values are the generated
-inputs themselves, which the oracle decoder reproduces bit for bit (pinned in
+Blobs of the single-tensor tests come from the oracle's encoder. The test of
+the library's encoder, the model paths (streamed, resident, stored, tiered:
+they encode through the library, as a user would) and the tensor past 2^32
+values (whose blob the oracle decoder checks on sampled chunks first) use the
+library's encoder. The expected values are always the generated inputs
+themselves, which the oracle decoder reproduces bit for bit (pinned in
 test_oracle_pins.py). Every comparison is exact (integer bit patterns).
 """
 import os
