@@ -148,8 +148,8 @@ int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len
  * complete prefix code of lengths <= 12 -- Kraft sum 1, or one symbol of
  * length 1 --, an exponent of x without a code, total_bits not the stream
  * length those lengths give x), AFX_E_UNSUPPORTED (n above 2^40),
- * AFX_E_BUFFER_TOO_SMALL (blob_bytes below the blob size). On an error the
- * blob's contents are unspecified. */
+ * AFX_E_BUFFER_TOO_SMALL (blob_bytes below the blob size),
+ * AFX_E_HOST_MEMORY. On an error the blob's contents are unspecified. */
 int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *shape,
                const uint8_t code_len[256], uint64_t total_bits, void *blob, size_t blob_bytes,
                int threads);
@@ -233,7 +233,7 @@ int afx_restore_gemm_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32
  * n_elems BF16 bit patterns into out (host memory, out_bytes >= 2 n), with
  * `threads` workers over chunks (<= 0: hardware thread count).
  * Errors: as afx_query; AFX_E_INVALID_ARG (NULL out with n > 0),
- * AFX_E_BUFFER_TOO_SMALL (out_bytes < 2 n). */
+ * AFX_E_BUFFER_TOO_SMALL (out_bytes < 2 n), AFX_E_HOST_MEMORY. */
 int afx_decode_host(const void *blob_host, size_t blob_bytes, uint16_t *out, size_t out_bytes, int threads);
 
 /* ---- Storage (host). "Why Weight Offloading Slows Inference" (section
@@ -251,9 +251,10 @@ int afx_decode_host(const void *blob_host, size_t blob_bytes, uint16_t *out, siz
  * its own page-aligned 4 MiB buffer and copies the requested part to dst
  * (the kernel refuses direct transfers into GPU-pinned host memory). On
  * error dst may be partly written.
- * Errors: AFX_E_INVALID_ARG (NULL path or dst, unknown flag),
- * AFX_E_UNSUPPORTED (the file system refuses O_DIRECT), AFX_E_IO (open or
- * read failed, or the file ends inside the range). */
+ * Errors: AFX_E_INVALID_ARG (NULL path or dst, unknown flag, offset +
+ * bytes above 2^63 - 1), AFX_E_UNSUPPORTED (the file system refuses
+ * O_DIRECT), AFX_E_IO (open or read failed, or the file ends inside the
+ * range), AFX_E_HOST_MEMORY (no bounce buffer for a direct read). */
 int afx_file_read(const char *path, uint64_t offset, uint64_t bytes, void *dst, int threads, unsigned flags);
 
 #ifdef __cplusplus
