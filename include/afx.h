@@ -137,7 +137,8 @@ const char *afx_status_str(int status);
 
 /* afx_encode_plan: histogram the exponents of x (n BF16 bit patterns), pick
  * the code lengths, and report the stream length and the blob size.
- * threads <= 0 picks the hardware thread count. */
+ * threads <= 0 picks the hardware thread count. Errors: AFX_E_INVALID_ARG
+ * (NULL pointer), AFX_E_UNSUPPORTED (n above 2^40), AFX_E_HOST_MEMORY. */
 int afx_encode_plan(const uint16_t *x, uint64_t n, int threads, uint8_t code_len[256],
                     uint64_t *total_bits, uint64_t *blob_bytes);
 
