@@ -1,28 +1,34 @@
 #!/usr/bin/env python3
 """Benchmark: restore losslessly coded BF16 weights on one MI355X.
 
-One step = one pass of the whole restore over one batch of synthetic coded
-weights already resident in HBM: the workload's tensors are decoded by one
-afx_decode_layer_async call (one kernel launch for up to 32 tensors).
+Default workload (`model`): the whole synthetic Qwen3-14B-shaped model, 40
+decoder layers plus the embedding, the untied output head and the final norm
+(42 units, 14.77G BF16 values, 29.5 GB restored), compressed in pinned host
+memory. One step is one pass of the restore over every unit with the
+compressed model resident in HBM: one afx_decode_layer_async call (one
+kernel launch) per unit, back to back on one stream, each unit into its own
+output region. The streamed pass (unit i+1 copied over the host link while
+unit i is restored, "Why Weight Offloading Slows Inference", section
+"Loading during computation"), the restore of one decoder layer and of the
+embedding inside the pass, and the CPU oracle on a bounded sample of the
+units are reported beside it.
 
-Default workload: one Qwen3-14B-shaped decoder layer (11 tensors, 330.3M
-BF16 values, 0.66 GB restored), the unit the time-to-ready model of "Why
-Weight Offloading Slows Inference" reasons about. Other workloads:
-tensor-1024 (1024x1024), q_proj (5120x5120), embedding (151936x5120), model
-(the whole 40-layer model, compressed in pinned host memory), disk (the
-whole model stored compressed in a file, read cold, copied and restored),
-tiers (the model spread over residency tiers under memory budgets) and gemv
-(the restore fused into the products y += W x of one layer's matrices).
+Other workloads: layer (one decoder layer, 11 tensors in one launch),
+tensor-1024 (1024x1024), q_proj (5120x5120), embedding (151936x5120), disk
+(the whole model stored compressed in a file, read cold, copied and
+restored), tiers (the model spread over residency tiers under memory
+budgets), gemv and gemm (the restore fused into the products of one layer's
+matrices) and token (one token's products over the whole model).
 
 Prints one JSON line with the throughput of restored BF16, the HBM roofline
 fraction of the decode kernel (hipEvent timing on the launch stream), and the
 CPU oracle's decode rate on this host as a baseline.
 
-Steps rotate over enough copies of the workload's blobs and outputs that a
-copy is touched again only after about 4 GB of other traffic, as in a pass
-over a model whose layers each pass once. Re-running one resident copy is
-faster (part of it is still cached) and is not what a model pass sees;
---copies 1 measures that case.
+The single-workload steps rotate over enough copies of the workload's blobs
+and outputs that a copy is touched again only after about 4 GB of other
+traffic, as in a pass over a model whose layers each pass once. Re-running
+one resident copy is faster (part of it is still cached) and is not what a
+model pass sees; --copies 1 measures that case.
 """
 from __future__ import annotations
 
@@ -62,6 +68,22 @@ def host_threads() -> int:
         return len(os.sched_getaffinity(0))
     except AttributeError:
         return os.cpu_count() or 1
+
+
+def cpu_share() -> int:
+    """Host threads this process may use: OMP_NUM_THREADS where the host sets
+    it (the share of the host's cores that goes with one GPU), else every
+    core in the affinity mask."""
+    try:
+        v = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        v = 0
+    return max(1, min(v, host_threads())) if v > 0 else host_threads()
+
+
+def host_cpu_facts() -> dict:
+    return {"affinity_cores": host_threads(), "os_cpu_count": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "threads_used": cpu_share()}
 
 
 def workload_specs(name: str):
@@ -110,7 +132,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer",
+    ap.add_argument("--workload", default="model",
                     choices=["layer", "tensor-1024", "q_proj", "embedding", "model", "disk", "tiers", "gemv", "gemm",
                              "token"])
     ap.add_argument("--m", type=int, default=None,
@@ -141,7 +163,7 @@ def main() -> int:
         return 2
     afx.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    threads = min(16, host_threads())
+    threads = cpu_share()
     if args.workload == "model":
         return bench_model(args, threads)
     if args.workload == "disk":
@@ -257,7 +279,7 @@ def main() -> int:
         cpu = {"value": round(2 * n_cpu / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"{passes} whole passes over the {workload} blobs ({n_total} values each), bit-serial "
                          f"canonical decode, chunk-parallel over {threads} threads; {cpu_s:.1f} CPU-s",
-               "seconds": round(t_cpu, 2),
+               "seconds": round(t_cpu, 2), "host": host_cpu_facts(),
                "one_thread": {"value": round(2 * n1 / t1 / 1e9, 3), "unit": "GB/s",
                               "sample": f"{n1} values of the workload's tensors in turn, one thread"}}
 
@@ -608,71 +630,168 @@ def bench_token(args, threads: int) -> int:
 
 
 def bench_model(args, threads: int) -> int:
-    """The whole synthetic model: 40 Qwen3-14B-shaped layers, the embedding,
-    the untied output head and the final norm (~29.5 GB BF16), compressed in
-    pinned host memory. `value` is the restore of the whole model with the
-    compressed model resident in HBM (one call and one launch per unit,
-    each unit into its own output region); the streamed run (copy of unit
-    i+1 over the host link overlapping the restore of unit i) is reported
-    beside it. Both are checked bit for bit on a separate pass."""
+    """The default workload: the whole synthetic model, 40 Qwen3-14B-shaped
+    layers, the embedding, the untied output head and the final norm (42
+    units, ~29.5 GB BF16), compressed in pinned host memory.
+
+    `value` is one pass of the restore over the whole model with its
+    compressed bytes resident in HBM (one call and one launch per unit, each
+    unit into its own output region). Beside it: the streamed pass (unit i+1
+    copied over the host link while unit i is restored), the restore of the
+    embedding (unit 0) and of layer 0 (unit 1) timed inside a resident pass,
+    and the CPU oracle on a bounded sample of the units.
+
+    Checks, off the clock: a streamed pass that runs free copies every
+    unit's restored output aside on the compute stream, and each copy is
+    compared with the unit's original bits generated again from its seeds;
+    the resident pass is compared with those copies; the oracle's decode of
+    the sampled units is compared with them too."""
     import torch
 
     from lossless_bf16_weight_afx_amd import ready, stream, synth
 
+    dev = torch.device("cuda:0")
     t0 = time.time()
-    units = stream.build_model(synth.model_units(args.layers), threads=threads, keep_raw=True, progress=log)
+    units = stream.build_model(synth.model_units(args.layers), threads=threads, progress=log)
     restored = 2 * sum(u.n_values for u in units)
     blob_total = sum(u.blob_bytes for u in units)
+    workload = f"qwen3-14b-model-{args.layers}-layers"
     log(f"[bench] model store ready in {time.time() - t0:.0f}s: {restored} B restored, {blob_total} B compressed")
+
+    # ---- checked streamed pass, running free: every unit's output copied
+    # aside after its restore, then compared with its original bits
     st = stream.Streamer(units)
-    ok = []
-    st.run(on_unit=lambda i, u, out: ok.append(stream.check_unit(u, out)))
+    snaps = [torch.empty(stream.unit_slots(u), dtype=torch.int16, device=dev) for u in units]
+    st.run(snapshot=snaps)
+    torch.cuda.synchronize()
+    t1 = time.time()
+    ok = [stream.check_unit_regen(u, sn, threads) for u, sn in zip(units, snaps)]
     exact = all(ok)
-    log(f"[bench] checked streamed pass: bit_exact={exact}")
+    log(f"[bench] checked streamed pass, {len(units)} units against their original bits "
+        f"({time.time() - t1:.0f}s): bit_exact={exact}" + ("" if exact else f" (bad units {[i for i, o in enumerate(ok) if not o]})"))
+
+    # ---- streamed passes, timed
     for _ in range(max(1, args.warmup)):
         st.run()
     runs = [st.run() for _ in range(max(1, args.steps))]
     e2e_ms = float(np.median([r["e2e_ms"] for r in runs]))
     dec_ms = float(np.median([sum(r["decode_ms"]) for r in runs]))
     link_ms = float(np.median([st.link_copy_ms() for _ in range(3)]))
+    t_dec_layer = float(np.median([r["decode_ms"][1] for r in runs])) * 1e-3
     del st
     torch.cuda.empty_cache()
-    res = stream.resident_decode(units, steps=max(1, args.steps), check=True)
+
+    # ---- the resident pass: `value`; checked against the streamed pass's
+    # copies, then timed (the whole pass between two events on the launch
+    # stream), then one more pass with an event between every two units
+    res = stream.resident_decode(units, steps=max(1, args.steps), check=True, reference=snaps,
+                                 warmup=max(1, args.warmup), per_unit=True)
     exact &= bool(res["bit_exact"])
-    log(f"[bench] checked resident pass: bit_exact={res['bit_exact']}")
-    for u in units:
-        u.raw = []  # free the originals
+    log(f"[bench] checked resident pass against the streamed one: bit_exact={res['bit_exact']}")
     resident_ms = res["ms"]
+    launches = res["launches"]
     value = restored / (resident_ms * 1e-3) / 1e9
+    alg = blob_total + restored
+    achieved = alg / (resident_ms * 1e-3) / 1e9
+
+    def unit_figures(k: int, name: str) -> dict:
+        u = units[k]
+        ms = res["unit_ms"][k]
+        a = u.blob_bytes + 2 * u.n_values
+        return {"unit": k, "name": name, "tensors": len(u.specs), "values": u.n_values,
+                "restored_bytes": 2 * u.n_values, "blob_bytes": u.blob_bytes, "us": round(ms * 1e3, 1),
+                "restored_GBps": round(2 * u.n_values / (ms * 1e-3) / 1e9, 1),
+                "roofline_frac": round(a / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    per_config = {"decoder_layer_0": unit_figures(1, "qwen3-14b-decoder-layer (layers.0, one launch)"),
+                  "embedding": unit_figures(0, "qwen3-14b-embedding-151936x5120 (one launch)")}
+
+    layer_alg = units[1].blob_bytes + 2 * units[1].n_values
+    copy_gbps, copy_each_way = copy_ceiling(torch.cuda.current_stream(dev), layer_alg, 4)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(workload),
+                "algorithmic_bytes_per_launch": round(alg / launches), "launches_per_step": launches,
+                "kernel": KERNEL_NAME, "kernel_ms": round(resident_ms / launches, 5),
+                "copy_ceiling_GBps": round(copy_gbps, 1), "calib_copy_bytes_each_way": copy_each_way}
+
     link_gbps = blob_total / (link_ms * 1e-3) / 1e9
     layer = units[1]
-    t_dec_layer = float(np.median([r["decode_ms"][1] for r in runs])) * 1e-3
     eq2 = {"saved_link_s_per_layer": round((2 * layer.n_values - layer.blob_bytes) / (link_gbps * 1e9), 6),
            "decode_s_per_layer": round(t_dec_layer, 6),
            "compression_pays": bool(ready.compression_pays(2 * layer.n_values, layer.blob_bytes,
                                                           link_gbps * 1e9, t_dec_layer))}
-    alg = blob_total + restored
+    streamed = {"ready_weight_GBps_e2e": round(restored / (e2e_ms * 1e-3) / 1e9, 1),
+                "decode_only_GBps": round(restored / (dec_ms * 1e-3) / 1e9, 1),
+                "e2e_ms": round(e2e_ms, 2), "decode_ms": round(dec_ms, 2),
+                "link_GBps_compressed_copy": round(link_gbps, 1),
+                "uncompressed_copy_equiv_ms": round(restored / (link_gbps * 1e9) * 1e3, 2),
+                "eq2_per_layer": eq2}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, ok_cpu = model_cpu_baseline(units, snaps, threads)
+        exact &= ok_cpu
+    del snaps
+    torch.cuda.empty_cache()
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(resident_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(resident_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u32", "data": "synthetic",
-        "config": {"workload": f"qwen3-14b-model-{args.layers}-layers", "units": len(units), "values": restored // 2,
+        "config": {"workload": workload, "units": len(units), "values": restored // 2,
                    "restored_bytes": restored, "blob_bytes": blob_total, "ratio": round(blob_total / restored, 4),
-                   "launches_per_pass": res["launches"]},
-        "bit_exact": bool(exact),
-        "roofline": {"bound": "hbm", "achieved": round(alg / (resident_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(alg / (resident_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": None, "kernel": KERNEL_NAME},
-        "streamed": {"ready_weight_GBps_e2e": round(restored / (e2e_ms * 1e-3) / 1e9, 1),
-                     "decode_only_GBps": round(restored / (dec_ms * 1e-3) / 1e9, 1),
-                     "e2e_ms": round(e2e_ms, 2), "decode_ms": round(dec_ms, 2),
-                     "link_GBps_compressed_copy": round(link_gbps, 1),
-                     "uncompressed_copy_equiv_ms": round(restored / (link_gbps * 1e9) * 1e3, 2),
-                     "eq2_per_layer": eq2},
-        "cpu_baseline": None,
+                   "launches_per_pass": launches, "encoder": "libafx afx_encode"},
+        "bit_exact": bool(exact), "roofline": roofline, "per_config": per_config, "streamed": streamed,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0 if exact else 1
+
+
+def model_cpu_baseline(units, snaps, threads: int):
+    """The CPU oracle's chunk-parallel decoder on a bounded sample of the
+    model's units (layer 0, the embedding, the head, then layers spread over
+    the model) until about 15 CPU-seconds are spent, on `threads` threads;
+    and the same decoder on one thread for about 3 seconds. Each sampled
+    unit's decode is compared with the GPU's restored copy."""
+    import oracle
+
+    order = [1, 0, len(units) - 1] + [k for k in range(2, len(units) - 1, 7)]
+    n_dec, t_dec, exact, sampled = 0, 0.0, True, []
+    cpu0 = time.process_time()
+    for k in order:
+        u = units[k]
+        gpu = snaps[k].cpu().numpy().view(np.uint16)
+        off = 0
+        for info, boff in zip(u.infos, u.offsets):
+            blob = u.host[boff:boff + int(info.blob_bytes)].numpy()
+            t0 = time.perf_counter()
+            d = oracle.decode(blob, threads=threads)
+            t_dec += time.perf_counter() - t0
+            n = int(info.n_elems)
+            exact &= bool(np.array_equal(d, gpu[off:off + n]))
+            off += (n + 127) // 128 * 128
+            n_dec += n
+        sampled.append(u.name)
+        if time.process_time() - cpu0 > 15.0:
+            break
+    cpu_s = time.process_time() - cpu0
+    n1, t1 = 0, 0.0
+    for info, boff in zip(units[1].infos, units[1].offsets):
+        blob = units[1].host[boff:boff + int(info.blob_bytes)].numpy()
+        t0 = time.perf_counter()
+        oracle.decode(blob, threads=1)
+        t1 += time.perf_counter() - t0
+        n1 += int(info.n_elems)
+        if t1 > 3.0:
+            break
+    cpu = {"value": round(2 * n_dec / t_dec / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"units {', '.join(sampled)} of the model ({n_dec} values, {2 * n_dec} B restored): bit-serial "
+                     f"canonical decode, chunk-parallel over {threads} threads; {cpu_s:.1f} CPU-s",
+           "seconds": round(t_dec, 2), "host": host_cpu_facts(),
+           "one_thread": {"value": round(2 * n1 / t1 / 1e9, 3), "unit": "GB/s",
+                          "sample": f"{n1} values of layers.0's tensors in turn, one thread"}}
+    return cpu, exact
 
 
 def bench_disk(args, threads: int) -> int:

@@ -241,6 +241,23 @@ int check_job(const afx_job &j) {
     return AFX_OK;
 }
 
+// The jobs of one call run in one launch: no job's output may share a byte
+// with another job's output or with any job's blob (check_job has compared
+// each output with its own blob). Quadratic, but batches are small.
+bool outputs_overlap(const afx_job *jobs, size_t n) {
+    for (size_t i = 0; i < n; ++i) {
+        const afx_job &a = jobs[i];
+        for (size_t k = 0; k < n; ++k) {
+            if (k == i) continue;
+            const afx_job &b = jobs[k];
+            if (ranges_overlap(a.out_dev, a.info->decoded_bytes, b.blob_dev, b.info->blob_bytes) ||
+                (k > i && ranges_overlap(a.out_dev, a.info->decoded_bytes, b.out_dev, b.info->decoded_bytes)))
+                return true;
+        }
+    }
+    return false;
+}
+
 TensorDesc describe(const afx_job &j) {
     const afx_info &I = *j.info;
     const uint8_t *b = static_cast<const uint8_t *>(j.blob_dev);
@@ -324,6 +341,7 @@ int afx_decode_layer_async(const afx_job *jobs, size_t n_jobs, void *stream) {
         const int rc = check_job(jobs[i]);
         if (rc != AFX_OK) return rc;
     }
+    if (outputs_overlap(jobs, n_jobs)) return AFX_E_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (size_t i = 0; i < n_jobs; i += AFX_MAX_JOBS_PER_LAUNCH) {
         const size_t k = std::min<size_t>(AFX_MAX_JOBS_PER_LAUNCH, n_jobs - i);

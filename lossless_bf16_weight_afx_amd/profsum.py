@@ -38,7 +38,7 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def _pmc(path, kernel):
+def _pmc(path, kernel, stat=statistics.median):
     per = collections.defaultdict(list)
     for r in _rows(path):
         per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
@@ -46,7 +46,7 @@ def _pmc(path, kernel):
     copy = [k for k in per if "bitwise_not" in k]
     if not mine or not copy:
         raise SystemExit(f"{path}: no dispatches of {kernel} or of the copy kernel")
-    return statistics.median(sum((per[k] for k in mine), [])), statistics.median(sum((per[k] for k in copy), []))
+    return stat(sum((per[k] for k in mine), [])), statistics.median(sum((per[k] for k in copy), []))
 
 
 def main(argv=None) -> int:
@@ -56,7 +56,11 @@ def main(argv=None) -> int:
     ap.add_argument("--tag", required=True, help="suffix of the run directories")
     ap.add_argument("--bench-args", required=True, help="bench.py arguments of the trace run")
     ap.add_argument("--pmc-bench-args", default=None, help="bench.py arguments of the counter runs, if others")
+    ap.add_argument("--stat", choices=["median", "mean"], default="median",
+                    help="statistic of the kernel's counters over its dispatches: the median for launches of one "
+                         "size, the mean for a pass of launches of different sizes (the whole model)")
     args = ap.parse_args(argv)
+    stat = statistics.mean if args.stat == "mean" else statistics.median
     sys.path.insert(0, ROOT)
     import bench
 
@@ -72,8 +76,8 @@ def main(argv=None) -> int:
     roof = line["roofline"]
     alg = int(roof["algorithmic_bytes_per_launch"])
     copy_bytes = int(roof.get("calib_copy_bytes_each_way") or (alg // 4) * 2)
-    f_k, f_c = _pmc(os.path.join(d, f"prof_fetch_{t}", "run_counter_collection.csv"), k)
-    w_k, w_c = _pmc(os.path.join(d, f"prof_write_{t}", "run_counter_collection.csv"), k)
+    f_k, f_c = _pmc(os.path.join(d, f"prof_fetch_{t}", "run_counter_collection.csv"), k, stat)
+    w_k, w_c = _pmc(os.path.join(d, f"prof_write_{t}", "run_counter_collection.csv"), k, stat)
     fs, ws = copy_bytes / (f_c * 1024), copy_bytes / (w_c * 1024)
     rd, wr = f_k * 1024 * fs, w_k * 1024 * ws
     workload = line["config"]["workload"]
@@ -88,7 +92,7 @@ def main(argv=None) -> int:
 # trace:  {cmd_t}
 # fetch:  {cmd_f}
 # write:  {cmd_w}
-# summary: python -m lossless_bf16_weight_afx_amd.profsum --kernel {k} --dir {d} --tag {t} --bench-args "{args.bench_args}"{f' --pmc-bench-args "{args.pmc_bench_args}"' if args.pmc_bench_args else ''}
+# summary: python -m lossless_bf16_weight_afx_amd.profsum --kernel {k} --dir {d} --tag {t} --bench-args "{args.bench_args}"{f' --pmc-bench-args "{args.pmc_bench_args}"' if args.pmc_bench_args else ''}{' --stat mean' if args.stat == 'mean' else ''}
 #
 # Kernel trace ({st['Calls']} dispatches of {k} in the run)
 kernel = {k}
@@ -100,7 +104,7 @@ max_duration_ns = {int(st['MaxNs'])}
 bench_ms_per_step = {line['ms_per_step']}
 bench_kernel_ms = {roof.get('kernel_ms')}
 #
-# HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch, median),
+# HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch, {args.stat} over the kernel's dispatches),
 # each scaled by what the same counter reads for torch's elementwise
 # bitwise_not over int16 (a plain copy kernel: {copy_bytes} B read, {copy_bytes} B written)
 fetch_kib_raw = {f_k:.1f}

@@ -112,9 +112,14 @@ class Streamer:
                 per_buf.append(afx.make_jobs(js))
             self.jobs.append(per_buf)
 
-    def run(self, on_unit=None) -> dict:
+    def run(self, on_unit=None, snapshot=None) -> dict:
         """Stream every unit once. ``on_unit(i, unit, out_tensor)`` is called
-        after unit i is restored (it synchronizes; use only off the clock)."""
+        after unit i is restored (it synchronizes; use only off the clock).
+        ``snapshot`` (a list of device int16 tensors, one of unit_slots(u)
+        elements per unit) receives a device-to-device copy of every unit's
+        restored output, ordered after its restore on the compute stream with
+        no host wait, so a pass that runs free (copies overlapping restores)
+        can be checked unit by unit afterwards."""
         torch = self.torch
         n = len(self.units)
         main = torch.cuda.current_stream(self.dev)
@@ -137,6 +142,10 @@ class Streamer:
             dec_start[i].record(main)
             afx.afx_decode_layer_async(self.jobs[i][b], main.cuda_stream)
             decoded[i].record(main)
+            if snapshot is not None:
+                # on the compute stream: the restore of unit i + 2 into the
+                # same buffer is ordered after this read
+                snapshot[i].copy_(self.out[b][:snapshot[i].numel()], non_blocking=True)
             if on_unit is not None:
                 decoded[i].synchronize()
                 on_unit(i, u, self.out[b])
@@ -160,6 +169,27 @@ class Streamer:
         return s.elapsed_time(e)
 
 
+def unit_slots(u: Unit) -> int:
+    """Output elements a unit occupies (every tensor's output 256-byte aligned)."""
+    return sum(_out_slot(int(i.n_elems)) for i in u.infos)
+
+
+def check_unit_regen(u: Unit, out, threads: int = 0) -> bool:
+    """Bit-exact check of a restored unit against its original bits,
+    generated again from the unit's seeded specs one tensor at a time (host
+    memory stays at one tensor)."""
+    import torch
+
+    off, ok = 0, True
+    for sp in u.specs:
+        x = synth.generate(sp, threads=threads or None)
+        ref = torch.from_numpy(x.view(np.int16)).to(out.device)
+        ok &= bool(torch.equal(out[off:off + x.size], ref))
+        del ref, x
+        off += _out_slot(sp.numel)
+    return ok
+
+
 def check_unit(u: Unit, out) -> bool:
     """Bit-exact check of a restored unit against its original bits."""
     import torch
@@ -172,19 +202,28 @@ def check_unit(u: Unit, out) -> bool:
     return ok
 
 
-def resident_decode(units, steps: int = 3, device="cuda", check: bool = False) -> dict:
+def resident_decode(units, steps: int = 3, device="cuda", check: bool = False, reference=None,
+                    warmup: int = 1, per_unit: bool = False, threads: int = 0) -> dict:
     """Restore the whole model with every unit's compressed bytes already in
     HBM, into one output region per unit (the restored model, ~29.5 GB, and
     the compressed one, ~20.5 GB, both fit in HBM): one afx_decode_layer_async
     call per unit, back to back on one stream. (Packing several layers into
     each 32-tensor launch is slower: mid-sized tensors then get too few or too
-    many whole workgroups.) Returns milliseconds per whole-model pass and, with
-    ``check``, whether every unit came back bit-exact (needs the raw bits)."""
+    many whole workgroups.)
+
+    Returns milliseconds per whole-model pass (``steps`` passes between two
+    events, after ``warmup`` passes) and, with ``check``, whether every unit
+    came back bit-exact: against ``reference`` (a list of device int16
+    tensors, one per unit, of unit_slots(u) elements, e.g. the snapshots of a
+    checked streamed pass) when given, else against the raw bits kept in the
+    units, else against bits generated again from the units' specs. With
+    ``per_unit`` one more pass records an event between every two units and
+    reports each unit's milliseconds."""
     import torch
 
     dev = torch.device(device)
     blobs = [u.host[:u.blob_bytes].to(dev) for u in units]
-    slots = [sum(_out_slot(int(i.n_elems)) for i in u.infos) for u in units]
+    slots = [unit_slots(u) for u in units]
     out = torch.empty(sum(slots), dtype=torch.int16, device=dev)
     calls, base = [], 0
     for k, u in enumerate(units):
@@ -196,15 +235,24 @@ def resident_decode(units, steps: int = 3, device="cuda", check: bool = False) -
         base += slots[k]
         calls.append(afx.make_jobs(jobs))
     s = torch.cuda.current_stream(dev)
-    for arr in calls:  # warm-up pass (also the checked one)
+    for arr in calls:  # first pass: the checked one
         afx.afx_decode_layer_async(arr, s.cuda_stream)
     torch.cuda.synchronize(dev)
     exact = None
     if check:
         exact, base = True, 0
         for k, u in enumerate(units):
-            exact &= check_unit(u, out[base:base + slots[k]])
+            got = out[base:base + slots[k]]
+            if reference is not None:
+                exact &= bool(torch.equal(got, reference[k][:slots[k]]))
+            elif u.raw:
+                exact &= check_unit(u, got)
+            else:
+                exact &= check_unit_regen(u, got, threads)
             base += slots[k]
+    for _ in range(max(0, warmup - 1)):
+        for arr in calls:
+            afx.afx_decode_layer_async(arr, s.cuda_stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for _ in range(steps):
@@ -213,6 +261,15 @@ def resident_decode(units, steps: int = 3, device="cuda", check: bool = False) -
     e1.record(s)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
+    unit_ms = None
+    if per_unit:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        evs[0].record(s)
+        for k, arr in enumerate(calls):
+            afx.afx_decode_layer_async(arr, s.cuda_stream)
+            evs[k + 1].record(s)
+        torch.cuda.synchronize(dev)
+        unit_ms = [evs[k].elapsed_time(evs[k + 1]) for k in range(len(calls))]
     del blobs, out
     launches = sum((len(a) + afx.MAX_JOBS_PER_LAUNCH - 1) // afx.MAX_JOBS_PER_LAUNCH for a in calls)
-    return {"ms": ms, "launches": launches, "bit_exact": exact}
+    return {"ms": ms, "launches": launches, "bit_exact": exact, "unit_ms": unit_ms}

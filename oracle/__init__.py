@@ -20,7 +20,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "afx_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# AFX_ORACLE_LIB names another build of afx_oracle.c to load instead (the
+# mutation check of the pins loads deliberately broken copies this way)
+_LIB = os.environ.get("AFX_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 LMAX = 12
 CHUNK = 4096
@@ -47,6 +49,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
+            if "AFX_ORACLE_LIB" in os.environ:
+                raise OSError(f"AFX_ORACLE_LIB names {_LIB}, which does not exist")
             build()
         L = ctypes.CDLL(_LIB)
         L.afx_oracle_layout.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _u64p]

@@ -114,6 +114,16 @@ def test_decode_argument_errors_before_any_hip_call(L):
     assert L.afx_decode_layer_async(jobs, 2, None) == afx.AFX_E_MISALIGNED
     assert L.afx_decode_layer_async(None, 3, None) == afx.AFX_E_INVALID_ARG
     assert L.afx_decode_layer_async(None, 0, None) == afx.AFX_OK
+    # jobs of one call run in one launch: an output may share no byte with
+    # another job's output or blob
+    out_b = fake_dev * 8
+    jobs = afx.make_jobs([(info, fake_dev, fake_dev * 4, 2 * n), (info, fake_dev * 4 + 4096, out_b, 2 * n)])
+    assert L.afx_decode_layer_async(jobs, 2, None) == afx.AFX_E_INVALID_ARG  # job 0 writes job 1's blob
+    jobs = afx.make_jobs([(info, fake_dev, fake_dev * 4, 2 * n), (info, fake_dev, fake_dev * 4 + 4096, 2 * n)])
+    assert L.afx_decode_layer_async(jobs, 2, None) == afx.AFX_E_INVALID_ARG  # outputs overlap
+    jobs = afx.make_jobs([(info, fake_dev, fake_dev * 8, 2 * n), (info, fake_dev, fake_dev * 12, 2 * n),
+                          (info, fake_dev * 12, fake_dev * 16, 2 * n)])
+    assert L.afx_decode_layer_async(jobs, 3, None) == afx.AFX_E_INVALID_ARG  # job 2's blob is job 1's output
 
 
 # ---------------------------------------------------------------------------

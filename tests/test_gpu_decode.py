@@ -255,13 +255,56 @@ def test_streamed_units_double_buffered():
     say("[gpu] case streamed units: checked pass")
     st.run(on_unit=lambda i, u, out: ok.append(stream.check_unit(u, out)))
     assert ok == [True] * len(units)
-    say("[gpu] case streamed units: free-running pass")
-    res = st.run()
+    say("[gpu] case streamed units: free-running pass, every unit copied aside")
+    snaps = [torch.empty(stream.unit_slots(u), dtype=torch.int16, device="cuda") for u in units]
+    res = st.run(snapshot=snaps)
     torch.cuda.synchronize()
+    assert [stream.check_unit(u, sn) for u, sn in zip(units, snaps)] == [True] * len(units)
     # the last two units are still in their buffers after a free-running pass
     assert stream.check_unit(units[-1], st.out[(len(units) - 1) % 2])
     assert stream.check_unit(units[-2], st.out[(len(units) - 2) % 2])
     assert res["e2e_ms"] > 0 and len(res["decode_ms"]) == len(units)
+
+
+def _box_threads() -> int:
+    try:
+        return max(1, int(os.environ.get("OMP_NUM_THREADS", "8")))
+    except ValueError:
+        return 8
+
+
+def test_full_model_streamed_every_unit_bit_exact():
+    """The whole 40-layer model at full size (42 units: the embedding, 40
+    Qwen3-14B-shaped layers, the output head with the final norm; 29.5 GB
+    restored from 20.5 GB compressed in pinned host memory), streamed with
+    the copy of each unit overlapping the restore of the one before, running
+    free. After each restore the unit's output is copied aside on the compute
+    stream (no host wait), and every copy is compared with the unit's
+    original bits, generated again unit by unit. The same model restored
+    with its compressed bytes resident in HBM must equal those copies."""
+    from lossless_bf16_weight_afx_amd import stream
+
+    threads = _box_threads()
+    say("[gpu] case full model: build the compressed store (42 units)")
+    units = stream.build_model(synth.model_units(), threads=threads, progress=say)
+    assert len(units) == 42
+    assert 2 * sum(u.n_values for u in units) == 29_536_614_400
+    st = stream.Streamer(units)
+    snaps = [torch.empty(stream.unit_slots(u), dtype=torch.int16, device="cuda") for u in units]
+    say("[gpu] case full model: free-running streamed pass with copies aside")
+    res = st.run(snapshot=snaps)
+    torch.cuda.synchronize()
+    assert len(res["decode_ms"]) == 42
+    del st
+    bad = []
+    for k, (u, sn) in enumerate(zip(units, snaps)):
+        if not stream.check_unit_regen(u, sn, threads):
+            bad.append((k, u.name))
+        say(f"[gpu] case full model: unit {k} {u.name} checked")
+    assert not bad, f"units restored wrong: {bad}"
+    say("[gpu] case full model: resident pass against the streamed one")
+    rres = stream.resident_decode(units, steps=1, check=True, reference=snaps)
+    assert rres["bit_exact"] is True and rres["launches"] == 42
 
 
 def test_resident_model_one_launch_per_unit():
