@@ -49,10 +49,9 @@ METRIC = "decoded BF16 GB/s on 1 MI355X + % of HBM roofline; bit-exact vs CPU or
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "lossless_bf16_weight_afx_amd", "csrc")
 KERNEL_NAME = "afx_decode_kernel"
-# the sources each kernel is built from (a profile taken on other sources is stale)
-KERNEL_SRCS = {"afx_decode_kernel": ("afx_decode.hip", "afx_device.h"),
-               "afx_gemv_kernel": ("afx_gemv.hip", "afx_device.h"),
-               "afx_gemm_kernel": ("afx_gemm.hip", "afx_device.h")}
+# the source each kernel is compiled from (a profile taken on other code is stale)
+KERNEL_SRCS = {"afx_decode_kernel": "afx_decode.hip", "afx_gemv_kernel": "afx_gemv.hip",
+               "afx_gemm_kernel": "afx_gemm.hip"}
 GEMV_METRIC = ("BF16 weight GB/s consumed by the fused restore+GEMV on 1 MI355X + % of HBM roofline; "
                "within the FP32 summation bound of the CPU oracle")
 GEMM_METRIC = ("BF16 weight GB/s consumed by the fused restore+GEMM (MFMA) on 1 MI355X + % of HBM roofline; "
@@ -101,11 +100,10 @@ def workload_specs(name: str):
 
 
 def kernel_sha(kernel: str = KERNEL_NAME) -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SRCS[kernel]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel's generated gfx950 code (build.device_code_sha)."""
+    from lossless_bf16_weight_afx_amd import build
+
+    return build.device_code_sha(KERNEL_SRCS[kernel])
 
 
 def profile_traffic(workload: str, kernel: str = KERNEL_NAME):

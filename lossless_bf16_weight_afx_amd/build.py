@@ -1,9 +1,12 @@
 """Compile libafx.so (HIP for gfx950 plus its host half) in-tree with hipcc."""
 from __future__ import annotations
 
+import functools
+import hashlib
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -26,6 +29,29 @@ def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
     return LIB
+
+
+@functools.lru_cache(maxsize=None)
+def device_code_sha(source: str) -> str:
+    """A hash of the gfx950 code that one kernel source compiles to: the
+    device assembly hipcc makes from csrc/<source> with the library's flags,
+    without comments, debug lines and the compiler's per-unit id. A profile
+    records it: edits that leave the code unchanged (comments, host-side
+    code) keep a profile valid, any change to the generated code makes it
+    stale."""
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        subprocess.run([HIPCC, *DEVICE_FLAGS, "-O3", "-std=c++17", "--cuda-device-only", "-S",
+                        "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, source), "-o", out],
+                       check=True, capture_output=True)
+        h = hashlib.sha256()
+        with open(out) as f:
+            for line in f:
+                t = line.split(";", 1)[0].strip()
+                if not t or t.startswith((".loc", ".file", ".ident")) or "__hip_cuid_" in t:
+                    continue
+                h.update(t.encode() + b"\n")
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

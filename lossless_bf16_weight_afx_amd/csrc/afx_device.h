@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "afx_index.h"
 #include "afx_internal.h"
 
 namespace afx {
@@ -46,18 +47,10 @@ struct LutScratch {
     uint8_t sorted[256];         // used symbols in (length, value) order
 };
 
-// Per-wave LDS: the chunk's code words while decoding, then its decoded
-// exponent bytes (4 KB) while storing. A chunk spans at most 4096 * 12 bits;
-// add the alignment slack of the start and the over-read of the last group.
-// Words are staged in reverse order (stream word j at index kRev - j), plus
-// one pad word above, so that one counter gives both the LDS address and the
-// funnel-shift amount of a 32-bit window (see Chain).
-constexpr uint32_t kStageWords = 1568;
-constexpr uint32_t kRev = kStageWords - 1;  // == 3 (mod 4): 16-byte aligned reversed stores
-static_assert(kRev % 4 == 3, "reversed staging needs kRev = 3 mod 4");
-// Each wave's slice, with the pad word, rounded up to 16 bytes so that every
-// slice starts 16-byte aligned.
-constexpr uint32_t kStageRow = (kStageWords + 1 + 3) & ~3u;
+// Per-wave LDS: the chunk's code words while decoding (kStageRow words,
+// staged in reverse; afx_index.h), then its decoded exponent bytes (4 KB)
+// while storing.
+static_assert(kStageRow * 4 >= kChunk, "a stage slice also holds a chunk's exponent bytes");
 
 // Rank of the k-th of nb workgroups that serve one tensor, counted XCD by
 // XCD. The grid's workgroups go to the 8 XCDs in turn (workgroup b to XCD
@@ -99,7 +92,7 @@ __device__ void build_lut(uint32_t len, void *table, LutScratch &S) {
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1), wave = s / kWave;
     uint32_t rank = 0;  // among same-length symbols of this wave with smaller value
-    if (len > kMaxLen) len = 0;  // only a corrupt blob gets here; treat as unused
+    len = used_length(len);  // only a corrupt blob has longer ones
     if (wave < kSymbolWaves) {
 #pragma unroll
         for (uint32_t l = 1; l <= kMaxLen; ++l) {
@@ -148,9 +141,7 @@ __device__ void build_lut(uint32_t len, void *table, LutScratch &S) {
 #pragma unroll
     for (uint32_t q = 1; q < kMaxLen; ++q) lim[q] = (uint32_t)__builtin_amdgcn_readlane((int)limit, (int)q);
     auto entry = [&](uint32_t idx) -> uint32_t {
-        uint32_t l = 1;
-#pragma unroll
-        for (uint32_t q = 1; q < kMaxLen; ++q) l += idx >= lim[q] ? 1u : 0u;
+        const uint32_t l = entry_length(idx, lim);
         const uint32_t j = S.base[l] + (idx >> (kMaxLen - l));
         return ((uint32_t)S.sorted[j & 255] << 8) | l;
     };
@@ -206,7 +197,7 @@ __device__ inline uint32_t sym_pair(uint32_t e1, uint32_t e2) { return __builtin
 // Bytes 0,1 of lo and of hi as the four bytes of a word.
 __device__ inline uint32_t join_halves(uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x05040100u); }
 
-__device__ inline uint32_t lookup(const uint16_t *lut, uint32_t win) { return lut[win >> (32 - kMaxLen)]; }
+__device__ inline uint32_t lookup(const uint16_t *lut, uint32_t win) { return lut[one_code_index(win)]; }
 
 // One decoding chain. With P the bit position in the staged words (MSB
 // first), the chain keeps r = 32 * kRev - P. Then the next 32 stream bits are
@@ -220,8 +211,8 @@ struct BufChain {
 };
 
 __device__ inline BufChain buf_chain(const uint32_t *stage, uint32_t r) {
-    const uint32_t *p = stage + (r >> 5);
-    return BufChain{r, r >> 5, p[1], p[0], p[-1]};
+    const uint32_t *p = stage + chain_word(r);
+    return BufChain{r, chain_word(r), p[1], p[0], p[-1]};
 }
 
 // Consume d bits (at most 24, so the window moves by at most one word).
@@ -229,7 +220,7 @@ __device__ inline BufChain buf_chain(const uint32_t *stage, uint32_t r) {
 // word read ahead.
 __device__ inline void buf_advance(BufChain &c, const uint32_t *stage, uint32_t d) {
     c.r -= d;
-    const uint32_t q = c.r >> 5;
+    const uint32_t q = chain_word(c.r);
     const bool moved = q != c.q;
     c.q = q;
     c.hi = moved ? c.lo : c.hi;
@@ -277,10 +268,9 @@ __device__ inline uint32_t complete_entry(uint32_t e, uint32_t e2) {
 // code bits sit at bits 29..18 of the window, and the pair table's byte
 // address (index times 4) is the window's high half-word masked: one
 // instruction.
-constexpr uint32_t kLead = 2;
 static_assert(kMaxLen + kLead + 2 == 16, "the table address is a masked high half-word");
 __device__ inline uint32_t pair_read(const uint32_t *plut, uint32_t win) {
-    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(plut) + ((win >> 16) & 0x3FFCu));
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(plut) + pair_offset(win));
 }
 
 // The buffered chains (BufChain, kLead bits behind) advanced through the
@@ -309,25 +299,6 @@ __device__ inline uint32_t join_entries(uint32_t first, uint32_t second) {
     return __builtin_amdgcn_perm(second, first, 0x06050201u);
 }
 
-__device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-
-// Where a chunk's code bits lie among the stream words.
-struct ChunkGeom {
-    uint64_t w0;      // first staged stream word (16-byte aligned)
-    uint32_t nwords;  // words to stage: through the chunk's last bit plus over-read slack
-    uint32_t rel;     // the chunk's first bit, counted from word w0
-};
-
-__device__ inline ChunkGeom chunk_geom(uint64_t base, uint64_t end) {
-    ChunkGeom g;
-    g.w0 = (base >> 5) & ~(uint64_t)3;
-    // unsigned arithmetic saturates through the min on a corrupt base pair
-    const uint64_t want = ((end + 31) >> 5) + 16 - g.w0;
-    g.nwords = (uint32_t)umin64(want, kStageWords);
-    g.rel = (uint32_t)(base - (g.w0 << 5));  // < 128
-    return g;
-}
-
 // The first 512 staged words of a chunk travel through registers so that
 // their loads can be issued one chunk ahead; longer chunks (more than about
 // 4 bits per element) fetch the rest when they are staged.
@@ -337,11 +308,9 @@ struct StreamRegs {
     uint4 v[2];
 };
 
-// Four stream words from 4-aligned index g. Past the end of the section the
-// index is clamped: such words lie beyond the last code bit (the stream ends
-// with four zero words), so what they hold never reaches an output.
+// Four stream words from 4-aligned index g (clamped to the section).
 __device__ inline uint4 load_words4(const TensorDesc &T, uint64_t g) {
-    return *reinterpret_cast<const uint4 *>(T.exp + umin64(g, T.last_word4));
+    return *reinterpret_cast<const uint4 *>(T.exp + word4_index(g, T.last_word4));
 }
 
 // Only the words the chunk needs are requested (typical chunks need ~350).
@@ -355,7 +324,7 @@ __device__ inline void load_stream(const TensorDesc &T, const ChunkGeom &g, int 
 
 // Stream word i goes to index kRev - i (reversed; see Chain).
 __device__ inline void put_words4(uint32_t *stage, uint32_t i, uint4 v) {
-    *reinterpret_cast<uint4 *>(stage + (kRev - 3 - i)) = make_uint4(v.w, v.z, v.y, v.x);
+    *reinterpret_cast<uint4 *>(stage + stage_put_index(i)) = make_uint4(v.w, v.z, v.y, v.x);
 }
 
 __device__ inline void put_stream(const TensorDesc &T, const ChunkGeom &g, const StreamRegs &s, uint32_t *stage,
@@ -390,11 +359,11 @@ struct Gaps {
 // Groups past the end of a short last chunk take the last group's gap: they
 // decode something, but nothing they decode is stored.
 __device__ inline Gaps load_gaps(const TensorDesc &T, uint64_t lc, int lane) {
-    const uint32_t ng = (uint32_t)((umin64(kChunk, T.n - lc * kChunk) + kGroup - 1) / kGroup);
+    const uint32_t ng = chunk_groups(T.n, lc);
     const uint16_t *gap = T.gap + lc * kGroupsPerChunk;
     // read once: not kept in the caches
-    return Gaps{__builtin_nontemporal_load(gap + min((uint32_t)lane, ng - 1)),
-                __builtin_nontemporal_load(gap + min((uint32_t)lane + kWave, ng - 1))};
+    return Gaps{__builtin_nontemporal_load(gap + gap_slot((uint32_t)lane, ng)),
+                __builtin_nontemporal_load(gap + gap_slot((uint32_t)lane + kWave, ng))};
 }
 
 // 16 output bytes; the output is written once and not read back here, so the
@@ -407,18 +376,13 @@ __device__ inline void store_out(uint16_t *p, uint4 v) {
 
 // Decode a staged chunk's 4096 exponent codes through the pair table and
 // leave the exponent bytes in element order at the start of `stage` (which
-// held the code words). Chain starts are clamped so that 32 decodes (at most
-// 384 bits) never leave the staged words even on a corrupt gap; the chains'
-// read ahead (one word past the window) stays at index >= 0 for the same
-// reason, and their windows (kLead bits behind) at most reach the pad word
-// above.
+// held the code words). Chain starts are clamped (chain_r0) so that the
+// chains stay inside the staged words and the pad word above even on a
+// corrupt gap.
 __device__ inline void decode_exponents(const ChunkGeom &g, const Gaps &gaps, const uint32_t *plut,
                                                uint32_t *stage, int lane) {
-    constexpr uint32_t kMaxStart = 32 * (kRev - 13);
-    // kLead bits behind the chain start: at most at bit 32 kRev + kLead,
-    // whose window's high word is the pad word above the staged words
-    const uint32_t ra = 32 * kRev - min(g.rel + gaps.a, kMaxStart) + kLead;
-    const uint32_t rb = 32 * kRev - min(g.rel + gaps.b, kMaxStart) + kLead;
+    const uint32_t ra = chain_r0(g.rel, gaps.a);
+    const uint32_t rb = chain_r0(g.rel, gaps.b);
     uint32_t wa[8], wb[8];
     BufChain A = buf_chain(stage, ra), B = buf_chain(stage, rb);
 #pragma unroll

@@ -46,16 +46,10 @@ constexpr uint32_t kRangeSlabs = 10;                         // a tile spans <= 
 constexpr uint32_t kRangeCols = kRangeSlabs * kSlabCols;
 constexpr uint32_t kMaxTokenBlocks = 2;                      // 32-token blocks per wave (1 or 2)
 constexpr uint32_t kRowsPerWave = kTileRows / kGemmWaves;    // 16
-// Code words staged per row segment: 256 codes of <= 12 bits (96 words), the
-// 16-byte alignment of the first word (3), the bit offset inside it and one
-// word of look-ahead for the last two-code window (2), rounded to 16 bytes.
-// They are staged in reverse order (stream word wa + i at index kSegRev - i),
-// so that the decoding chains of afx_device.h apply; a row's slice has one
-// more word above kSegRev for their reads.
-constexpr uint32_t kSegWords = 104;
-constexpr uint32_t kSegRev = kSegWords - 1;                  // == 3 (mod 4): aligned reversed stores
-constexpr uint32_t kSegRow = kSegWords + 4;                  // words per row slice
-static_assert(kSegRev % 4 == 3, "reversed staging needs kSegRev = 3 mod 4");
+// A row segment's code words (kSegWords, staged in reverse in a slice of
+// kSegRow words: afx_index.h), so that the decoding chains of afx_device.h
+// apply.
+static_assert(kSegWords * 32 >= kSlabCols * kMaxLen + 5 * 32, "a segment's words fit its slice");
 constexpr uint32_t kSlabStride = kSlabCols * 2 + 16;         // bytes per restored row in LDS
 
 struct GemmJob {
@@ -83,19 +77,19 @@ __device__ inline bf16x8 load_a(const uint16_t *p, bool ok) {
 // Stage four stream words (those at wa + i .. wa + i + 3) of a row segment,
 // reversed: stream word wa + j goes to index kSegRev - j.
 __device__ inline void put_seg4(uint32_t *seg, uint32_t i, uint4 v) {
-    *reinterpret_cast<uint4 *>(seg + (kSegRev - 3 - i)) = make_uint4(v.w, v.z, v.y, v.x);
+    *reinterpret_cast<uint4 *>(seg + seg_put_index(i)) = make_uint4(v.w, v.z, v.y, v.x);
 }
 
-// Decode the 32 exponent codes of the lane's two groups, which start at bit
-// offsets P1 and P2 of the row's staged segment (two interleaved buffered
-// chains); ex1[j], ex2[j] receive the exponent bytes of elements 4j..4j+3.
-// A chain start stays low enough that 32 codes of <= 12 bits, and the
-// chains' read-ahead, remain inside the slice even on a corrupt stream.
-__device__ inline void decode_groups(const uint32_t *seg, uint32_t P1, uint32_t P2, const uint16_t *lut,
+// Decode the 32 exponent codes of the lane's two groups, whose chains start
+// at counters r1 and r2 of the row's staged segment (two interleaved
+// buffered chains); ex1[j], ex2[j] receive the exponent bytes of elements
+// 4j..4j+3. The starts come clamped (seg_chain_r0), so that 32 codes of <=
+// 12 bits, and the chains' read-ahead, remain inside the slice even on a
+// corrupt stream.
+__device__ inline void decode_groups(const uint32_t *seg, uint32_t r1, uint32_t r2, const uint16_t *lut,
                                      uint32_t (&ex1)[8], uint32_t (&ex2)[8]) {
-    constexpr uint32_t kMaxStart = 32 * (kSegRev - 13);
-    BufChain A = buf_chain(seg, 32 * kSegRev - min(P1, kMaxStart));
-    BufChain B = buf_chain(seg, 32 * kSegRev - min(P2, kMaxStart));
+    BufChain A = buf_chain(seg, r1);
+    BufChain B = buf_chain(seg, r2);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         uint32_t a01, b01, a23, b23;
@@ -152,9 +146,8 @@ struct SlabData {
 __device__ inline SlabData slab_data(const TensorDesc &T, uint64_t e_seg, uint32_t q4, const SlabBits &b) {
     SlabData d;
     const uint64_t p_lo = quad_first(bit1(b)), p_hi = bit_end(b);
-    d.wa = (p_lo >> 5) & ~3ull;
-    const uint64_t need = p_hi >= p_lo ? ((p_hi + 31) >> 5) + 1 - d.wa : 0;  // corrupt: stage nothing
-    d.nw = (uint32_t)umin64(need, kSegWords);
+    d.wa = seg_first_word(p_lo);
+    d.nw = seg_words(p_lo, p_hi);
     // (words past the segment's end are staged too, and never read)
     d.w0 = load_words4(T, d.wa + 4 * q4);
     d.w1 = load_words4(T, d.wa + 16 + 4 * q4);
@@ -276,8 +269,8 @@ void afx_gemm_kernel(const GemmBatch batch) {
         }
         wave_sync();
         uint32_t ex1[8], ex2[8];
-        decode_groups(seg, (uint32_t)umin64(bit1(bits_c) - 32 * data_c.wa, 32 * kSegRev),
-                      (uint32_t)umin64(bit2(bits_c) - 32 * data_c.wa, 32 * kSegRev), lut, ex1, ex2);
+        decode_groups(seg, seg_chain_r0(bit1(bits_c), data_c.wa), seg_chain_r0(bit2(bits_c), data_c.wa), lut, ex1,
+                      ex2);
         // Join and put both groups into the slab.
         const uint32_t b1[8] = {data_c.s1a.x, data_c.s1a.y, data_c.s1a.z, data_c.s1a.w,
                                 data_c.s1b.x, data_c.s1b.y, data_c.s1b.z, data_c.s1b.w};

@@ -11,7 +11,8 @@ The summary gives the kernel's average launch duration from the trace, and
 its HBM bytes per launch from the two counters (KiB per dispatch), each
 scaled by what the same counter reads for the plain copy kernel of known size
 that bench.py runs (torch's bitwise_not over int16). It records a hash of the
-kernel's sources, so that a reader can tell when the profile is stale.
+kernel's generated gfx950 code (build.device_code_sha), so that a reader can
+tell when the profile is stale.
 
     python -m lossless_bf16_weight_afx_amd.profsum --kernel afx_decode_kernel \\
         --dir D --tag T --bench-args "--workload layer --steps 20 --warmup 3 --no-cpu-baseline"

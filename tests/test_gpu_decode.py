@@ -132,6 +132,74 @@ def test_misaligned_output_rejected():
     assert torch.all(out == 7).item()
 
 
+def _damage(blob: np.ndarray, what: str, rng) -> np.ndarray:
+    """A copy of blob with one section damaged as a stale or corrupted
+    device copy might be: random bit flips (high bits included) in the chunk
+    bases, random gaps, random code words, random code lengths (0..255), or
+    all of them at once."""
+    s = oracle.sections(blob)["offsets"]
+    n_chunks = -(-int(oracle.sections(blob)["header"]["n"]) // 4096)
+    c = blob.copy()
+
+    def flip(lo, hi, k):
+        idx = rng.integers(lo, hi, k)
+        c[idx] ^= (np.uint8(1) << rng.integers(0, 8, k).astype(np.uint8))
+
+    if what in ("bases", "all"):
+        flip(s["chunk_base"], s["chunk_base"] + 8 * (n_chunks + 1), max(4, n_chunks))
+    if what in ("gaps", "all"):
+        lo, hi = s["gap"], s["signmant"]
+        c[lo:hi] = rng.integers(0, 256, hi - lo, dtype=np.uint8)
+    if what in ("words", "all"):
+        lo, hi = s["exp"], s["blob_bytes"]
+        c[lo:hi] = rng.integers(0, 256, hi - lo, dtype=np.uint8)
+    if what in ("lengths", "all"):
+        c[s["code_len"]:s["code_len"] + 256] = rng.integers(0, 256, 256, dtype=np.uint8)
+    return c
+
+
+@pytest.mark.parametrize("what", ["bases", "gaps", "words", "lengths", "all"])
+def test_corrupt_device_blob_stays_in_bounds(what):
+    """A device blob that differs from the host copy afx_query validated
+    restores to wrong bits, never out of bounds: AFX_OK, the guard words
+    before and after the output untouched, and a good tensor restored in the
+    same launch still exact. (The index arithmetic behind this is checked
+    on the CPU by test_index_bounds.py.)"""
+    rng = np.random.default_rng(["bases", "gaps", "words", "lengths", "all"].index(what) + 90)
+    xs = [synth.generate(synth.TensorSpec("c0", (3 * 4096 + 77,), "normal", 91)),
+          synth.generate(synth.TensorSpec("c1", (256, 4096), "t4", 92))]
+    good = synth.generate(synth.TensorSpec("good", (5000, 33), "normal", 93))
+    guard = 128  # elements (256 bytes) of guard words before and after each output
+    say(f"[gpu] case corrupt device blob: {what}")
+    for x in xs:
+        blob = oracle.encode(x)
+        info = afx.afx_query(blob)  # the undamaged host copy
+        bad = _damage(blob, what, rng)
+        dev = afx.to_device(bad)
+        n = x.size
+        out = torch.full((n + 2 * guard,), 0x5A5A, dtype=torch.int16, device="cuda")
+        gblob = oracle.encode(good)
+        ginfo = afx.afx_query(gblob)
+        gdev = afx.to_device(gblob)
+        gout = torch.full((good.size + 2 * guard,), 0x5A5A, dtype=torch.int16, device="cuda")
+        jobs = afx.make_jobs([(info, dev.data_ptr(), out.data_ptr() + 2 * guard, 2 * n),
+                              (ginfo, gdev.data_ptr(), gout.data_ptr() + 2 * guard, 2 * good.size)])
+        afx.afx_decode_layer_async(jobs, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.all(o[:guard] == 0x5A5A) and np.all(o[guard + n:] == 0x5A5A), "wrote outside the output"
+        g = gout.cpu().numpy()
+        assert np.all(g[:guard] == 0x5A5A) and np.all(g[guard + good.size:] == 0x5A5A)
+        assert np.array_equal(g[guard:guard + good.size].view(np.uint16), good), "good tensor of the batch damaged"
+        # the same damaged blob through the blocking call
+        afx.afx_decode_tensor(info, dev.data_ptr(), out.data_ptr() + 2 * guard, 2 * n,
+                              torch.cuda.current_stream().cuda_stream)
+        o = out.cpu().numpy()
+        assert np.all(o[:guard] == 0x5A5A) and np.all(o[guard + n:] == 0x5A5A), "wrote outside the output"
+        if what in ("words", "all"):
+            assert not np.array_equal(o[guard:guard + n].view(np.uint16), x)  # it did decode something else
+
+
 def layer_blobs(layer=0):
     specs = synth.decoder_layer(layer)
     xs, blobs = [], []

@@ -1,6 +1,7 @@
 """The committed rocprofv3 summaries describe the kernel sources as they are.
 
-Each summary records a hash of its kernel's sources; bench.py reports a
+Each summary records a hash of its kernel's generated gfx950 code (the
+device assembly of its source, comments aside); bench.py reports a
 profile's HBM traffic only while that hash matches. A summary whose hash no
 longer matches was taken on other code and must be retaken, not kept.
 """
