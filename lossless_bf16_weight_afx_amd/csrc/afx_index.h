@@ -121,79 +121,6 @@ constexpr uint32_t entry_length(uint32_t idx, const uint32_t (&lim)[kMaxLen]) {
     return l;
 }
 
-// ---- sharing a launch's chunks among its workgroups ------------------------
-// The chunks of a launch's tensors, laid end to end (tensor t at slots
-// [F_t, F_t + n_t)), are cut into equal slices of S slots, one per
-// workgroup (the last may be shorter), so every workgroup restores the same
-// number of chunks however the tensors' sizes fall. Within a tensor the
-// chunks are not handed out as contiguous ranges: they go round the
-// tensor's workgroups (all of whose slices lie in it, "full", plus at most
-// two whose slices it shares with the tensor before or after, "partial"),
-// so that at any moment the tensor's workgroups stream one narrow band of
-// each of its arrays. In round j every workgroup with more than j chunks of
-// the tensor takes one; the full ones come first, counted XCD by XCD.
-
-// Rank of the k-th of nb workgroups, counted XCD by XCD. The grid's
-// workgroups go to the 8 XCDs in turn (workgroup b to XCD b mod 8) and each
-// XCD has its own L2; consecutive ranks take neighbouring chunks, which share
-// the cache lines at the ends of their code words, so those lines are then
-// mostly fetched by one XCD. A permutation of 0..nb-1.
-constexpr uint32_t xcd_rank(uint32_t k, uint32_t nb) {
-    constexpr uint32_t kXcds = 8;
-    const uint32_t x = k % kXcds, i = k / kXcds;
-    return x * (nb / kXcds) + umin32(x, nb % kXcds) + i;
-}
-
-// One workgroup's share of one tensor.
-struct Share {
-    uint64_t m;      // the tensor's full workgroups (S chunks each)
-    uint64_t qx;     // chunks of the first partial workgroup (rank m), 0 if none
-    uint64_t qy;     // chunks of the second (rank m + 1), qy <= qx, 0 if none
-    uint64_t rank;   // this workgroup's rank among the tensor's workgroups
-    uint64_t quota;  // chunks of the tensor this workgroup restores (0: none)
-};
-
-// The share of workgroup w (slice [wS, wS + S)) in the tensor at slots
-// [F, F + n), n >= 1, S >= 1.
-constexpr Share tensor_share(uint64_t F, uint64_t n, uint64_t S, uint64_t w) {
-    Share sh{};
-    const uint64_t end = F + n;
-    const uint64_t wa = F / S, wb = (end - 1) / S;  // first and last workgroup with slots of the tensor
-    const uint64_t qa = umin64((wa + 1) * S, end) - F;   // chunks of workgroup wa
-    const uint64_t qb = wa == wb ? 0 : end - wb * S;      // chunks of workgroup wb (when not wa)
-    const bool pa = qa < S, pb = wa != wb && qb < S;      // partial ends
-    const uint64_t fa = pa ? wa + 1 : wa, fb = pb ? wb : wb + 1;  // full workgroups [fa, fb)
-    sh.m = fb > fa ? fb - fa : 0;
-    // the partial ones: the larger share first (ties: the first workgroup)
-    uint64_t px = 0, py = 0, wx = ~(uint64_t)0, wy = ~(uint64_t)0;
-    if (pa && pb) {
-        const bool a_first = qa >= qb;
-        px = a_first ? qa : qb, wx = a_first ? wa : wb;
-        py = a_first ? qb : qa, wy = a_first ? wb : wa;
-    } else if (pa) {
-        px = qa, wx = wa;
-    } else if (pb) {
-        px = qb, wx = wb;
-    }
-    sh.qx = px;
-    sh.qy = py;
-    if (w >= fa && w < fb) {
-        sh.rank = xcd_rank((uint32_t)(w - fa), (uint32_t)sh.m);
-        sh.quota = S;
-    } else if (w == wx) {
-        sh.rank = sh.m, sh.quota = px;
-    } else if (w == wy) {
-        sh.rank = sh.m + 1, sh.quota = py;
-    }
-    return sh;
-}
-
-// The tensor's chunk that is this workgroup's k-th (k < quota): rounds
-// before k hand out m + [k > ...] chunks each, then this rank's place.
-constexpr uint64_t share_chunk(const Share &sh, uint64_t k) {
-    return k * sh.m + umin64(k, sh.qx) + umin64(k, sh.qy) + sh.rank;
-}
-
 // ---- the MFMA product's row segments --------------------------------------
 // Code words staged per row segment of 256 elements: 256 codes of <= 12 bits
 // (96 words), the 16-byte alignment of the first word (3), the bit offset
