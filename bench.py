@@ -55,7 +55,7 @@ KERNEL_SRCS = {"afx_decode_kernel": "afx_decode.hip", "afx_gemv_kernel": "afx_ge
 GEMV_METRIC = ("BF16 weight GB/s consumed by the fused restore+GEMV on 1 MI355X + % of HBM roofline; "
                "within the FP32 summation bound of the CPU oracle")
 GEMM_METRIC = ("BF16 weight GB/s consumed by the fused restore+GEMM (MFMA) on 1 MI355X + % of HBM roofline; "
-               "within twice the FP32 summation bound of the CPU oracle")
+               "within the FP32 summation bound of the CPU oracle")
 
 
 def log(*a):
@@ -361,7 +361,7 @@ def bench_gemv(args, threads: int) -> int:
         raise SystemExit("--m must be at least 1")
     kernel = "afx_gemm_kernel" if gemm else "afx_gemv_kernel"
     launch = afx.afx_restore_gemm_batch_async if gemm else afx.afx_restore_gemv_batch_async
-    tol = 2.0 if gemm else 1.0  # the matrix instructions' rounding is not documented: one ulp per addition
+    tol = 1.0  # the summation bound (for the matrix instruction, as measured by test_one_matrix_instruction_rounding)
     specs = [sp for sp in synth.decoder_layer(0) if len(sp.shape) == 2]
     workload = f"qwen3-14b-decoder-layer-{args.workload}-m{m}"
     t0 = time.time()

@@ -5,10 +5,14 @@ float64 product of the restored matrix.
 Small-integer weights and activations keep every partial sum exact in FP32,
 so there the result must equal the oracle's exactly, whatever the order of
 the sums: any indexing mistake (a transposed tile, a wrong slab, a lane
-layout) shows. Other data are checked within twice the classical bound of
-FP32 summation, gamma_(k-1) * sum |terms| (the matrix instructions' internal
-rounding is not documented; twice the bound allows one unit in the last place
-per addition instead of half of one)."""
+layout) shows. Other data are checked within the classical bound of FP32
+summation, gamma_(k-1) * sum |terms|. The matrix instruction's internal
+rounding is not documented; test_one_matrix_instruction_rounding measures
+it through this product: one instruction (16 products added to an FP32
+value) errs by at most a few units u * sum |terms|, inside gamma_16 of an
+FP32 sum of its 17 terms in any order, so a product over k columns made of
+k/16 such steps stays inside gamma_(k-1) * sum |terms|. Each test reports
+its worst error / bound."""
 import sys
 
 import numpy as np
@@ -72,9 +76,42 @@ def check(blob, rows, cols, x, m, y0=None):
     ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4,
                                      y0=None if y0 is None else y0.cpu().numpy())
     err = np.abs(got - ref)
-    worst = float(np.max(err / np.maximum(2 * bound, 1e-300)))
-    assert np.all(err <= 2 * bound), f"error above twice the bound: worst ratio {worst}"
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    say(f"[gpu]   worst error / bound = {worst:.3g}")
+    assert np.all(err <= bound), f"error above the bound: worst ratio {worst}"
     return worst
+
+
+def test_one_matrix_instruction_rounding():
+    """The rounding of one v_mfma_f32_32x32x16_bf16 step, measured through the
+    product: only the first 16 columns of W are nonzero, so every y[t, r] is
+    y0[t, r] plus one instruction's 16 products (the later steps add exact
+    zeros). Values span 2^-10..2^10 with random signs and y0 is as large as
+    the sums, so the sums cancel. The error of each output must stay within
+    gamma_16 * (sum |products| + |y0|), the bound of FP32 summation of its 17
+    terms in any order (products of two BF16 values are exact in FP32)."""
+    rows, cols, m = 128, 256, 256
+    rng = np.random.default_rng(5)
+    w = np.zeros((rows, cols), np.float32)
+    w[:, :16] = rng.standard_normal((rows, 16)) * np.exp2(rng.integers(-10, 10, (rows, 16)))
+    wb = synth.f32_to_bf16_bits(w.ravel())
+    x = synth.f32_to_bf16_bits((rng.standard_normal((m, cols)) * np.exp2(rng.integers(-10, 10, (m, cols))))
+                               .astype(np.float32))
+    y0 = torch.from_numpy((rng.standard_normal((m, rows)) * 1e3).astype(np.float32)).to("cuda")
+    blob = oracle.encode(wb, (rows, cols))
+    say("[gpu] case one matrix instruction's rounding")
+    got = gemm(blob, rows, cols, x, m, y0)
+    wf = synth.bf16_bits_to_f32(wb).astype(np.float64).reshape(rows, cols)[:, :16]
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64).reshape(m, cols)[:, :16]
+    c = y0.cpu().numpy().astype(np.float64)
+    exact = xf @ wf.T + c  # float64: the 16 exact products and y0, up to float64 rounding
+    terms = np.abs(xf) @ np.abs(wf).T + np.abs(c)
+    u = 2.0 ** -24
+    ratio = np.abs(got - exact) / (u * terms)
+    one_rounding = np.mean(got == exact.astype(np.float32).astype(np.float64))
+    say(f"[gpu]   max error / (u * sum |terms|) = {ratio.max():.3g} (gamma_16 = 16); equal to one rounding of "
+        f"the exact sum in {one_rounding:.3f} of {ratio.size} outputs")
+    assert ratio.max() <= 16 / (1 - 16 * u)
 
 
 @pytest.mark.parametrize("rows,cols,m,dist", [
@@ -87,8 +124,7 @@ def test_random_data_within_bound(rows, cols, m, dist):
     say(f"[gpu] case gemm {dist} {rows}x{cols} m={m}")
     w = synth.generate(synth.TensorSpec("w", (rows, cols), dist, rows + cols + m))
     x = synth.f32_to_bf16_bits(np.random.default_rng(m).standard_normal((m, cols)).astype(np.float32))
-    worst = check(oracle.encode(w, (rows, cols)), rows, cols, x, m)
-    say(f"[gpu]   worst error / (2 bound) = {worst:.3g}")
+    check(oracle.encode(w, (rows, cols)), rows, cols, x, m)
 
 
 def test_twelve_bit_codes_and_a_starting_y():
@@ -145,7 +181,8 @@ def test_layer_batch_one_launch():
     for (blob, x, y, _, _, _), sp in zip(keep, specs):
         ref, bound = oracle.restore_gemv(blob, sp.shape[0], sp.shape[1], x, threads=16)
         err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
-        assert np.all(err <= 2 * bound), sp.name
+        say(f"[gpu]   {sp.name}: worst error / bound = {float(np.max(err / np.maximum(bound, 1e-300))):.3g}")
+        assert np.all(err <= bound), sp.name
 
 
 def test_batches_over_sixteen_matrices():
@@ -159,7 +196,7 @@ def test_batches_over_sixteen_matrices():
         blob = oracle.encode(w, (rows, cols))
         mats.append((blob, rows, cols, afx.afx_query(blob), afx.to_device(blob)))
     for name, m, call, tol in [("gemv", 4, afx.afx_restore_gemv_batch_async, 1.0),
-                               ("gemm", 5, afx.afx_restore_gemm_batch_async, 2.0)]:
+                               ("gemm", 5, afx.afx_restore_gemm_batch_async, 1.0)]:
         say(f"[gpu] case {name} batch of 18 matrices, m={m}")
         jobs, keep = [], []
         for blob, rows, cols, info, db in mats:
