@@ -34,7 +34,9 @@
 // each lane.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include "afx_device.h"
 
@@ -241,21 +243,38 @@ int check_job(const afx_job &j) {
     return AFX_OK;
 }
 
-// The jobs of one call run in one launch: no job's output may share a byte
-// with another job's output or with any job's blob (check_job has compared
-// each output with its own blob). Quadratic, but batches are small.
-bool outputs_overlap(const afx_job *jobs, size_t n) {
-    for (size_t i = 0; i < n; ++i) {
-        const afx_job &a = jobs[i];
-        for (size_t k = 0; k < n; ++k) {
-            if (k == i) continue;
-            const afx_job &b = jobs[k];
-            if (ranges_overlap(a.out_dev, a.info->decoded_bytes, b.blob_dev, b.info->blob_bytes) ||
-                (k > i && ranges_overlap(a.out_dev, a.info->decoded_bytes, b.out_dev, b.info->decoded_bytes)))
-                return true;
-        }
+// The jobs of one call may run in one launch: no job's output may share a
+// byte with another job's output or with any job's blob (check_job has
+// compared each output with its own blob). Sorted by address, the outputs
+// must be disjoint, and each blob must miss the output that starts last at
+// or below its end (the outputs being disjoint, that is the only one that
+// can reach into it). O(n log n): a whole model's tensors in one call.
+// Returns -1 when host memory for the sort cannot be had.
+int outputs_overlap(const afx_job *jobs, size_t n) {
+    struct Range {
+        uintptr_t lo, hi;  // [lo, hi)
+    };
+    std::vector<Range> outs;
+    try {
+        outs.reserve(n);
+    } catch (...) {
+        return -1;
     }
-    return false;
+    for (size_t i = 0; i < n; ++i) {
+        const uintptr_t o = reinterpret_cast<uintptr_t>(jobs[i].out_dev);
+        if (jobs[i].info->decoded_bytes) outs.push_back(Range{o, o + jobs[i].info->decoded_bytes});
+    }
+    std::sort(outs.begin(), outs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < outs.size(); ++i)
+        if (outs[i].lo < outs[i - 1].hi) return 1;
+    for (size_t i = 0; i < n; ++i) {
+        if (!jobs[i].info->n_elems) continue;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(jobs[i].blob_dev), b1 = b0 + jobs[i].info->blob_bytes;
+        // the last output starting below the blob's end
+        auto it = std::lower_bound(outs.begin(), outs.end(), b1, [](const Range &r, uintptr_t v) { return r.lo < v; });
+        if (it != outs.begin() && std::prev(it)->hi > b0) return 1;
+    }
+    return 0;
 }
 
 TensorDesc describe(const afx_job &j) {
@@ -283,11 +302,19 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
     batch.n_tensors = 0;
     uint64_t total = 0;
     uint64_t first[AFX_MAX_JOBS_PER_LAUNCH];
-    for (size_t i = 0; i < n_jobs; ++i) {
-        if (jobs[i].info->n_elems == 0) continue;
-        first[batch.n_tensors] = total;
-        batch.t[batch.n_tensors++] = describe(jobs[i]);
-        total += jobs[i].info->n_chunks;
+    // Tensors of fewer chunks than a workgroup has waves (a layer's norm
+    // vectors) go last: together they are then a sliver of the grid's last
+    // share, served by a workgroup of their own (each tensor a workgroup
+    // serves costs it a table build), not added to one that also serves a
+    // share of a large tensor.
+    for (int pass = 0; pass < 2; ++pass) {
+        for (size_t i = 0; i < n_jobs; ++i) {
+            const uint64_t nc = jobs[i].info->n_chunks;
+            if (nc == 0 || (pass == 0) != (nc >= kWavesPerBlock)) continue;
+            first[batch.n_tensors] = total;
+            batch.t[batch.n_tensors++] = describe(jobs[i]);
+            total += nc;
+        }
     }
     if (total == 0) return AFX_OK;
     int max_blocks = 0;
@@ -318,6 +345,28 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
                : AFX_E_HIP;
 }
 
+// Every check of a batch call's jobs.
+int check_batch(const afx_job *jobs, size_t n_jobs) {
+    if (!jobs && n_jobs) return AFX_E_INVALID_ARG;
+    for (size_t i = 0; i < n_jobs; ++i) {
+        const int rc = check_job(jobs[i]);
+        if (rc != AFX_OK) return rc;
+    }
+    const int ov = outputs_overlap(jobs, n_jobs);
+    if (ov != 0) return ov < 0 ? AFX_E_HOST_MEMORY : AFX_E_INVALID_ARG;
+    return AFX_OK;
+}
+
+// The launches of a checked batch call.
+int decode_batch(const afx_job *jobs, size_t n_jobs, hipStream_t s) {
+    for (size_t i = 0; i < n_jobs; i += AFX_MAX_JOBS_PER_LAUNCH) {
+        const size_t k = std::min<size_t>(AFX_MAX_JOBS_PER_LAUNCH, n_jobs - i);
+        const int rc = launch(jobs + i, k, s);
+        if (rc != AFX_OK) return rc;
+    }
+    return AFX_OK;
+}
+
 }  // namespace
 }  // namespace afx
 
@@ -336,19 +385,8 @@ int afx_decode_tensor(const afx_info *info, const void *blob_dev, void *out_dev,
 }
 
 int afx_decode_layer_async(const afx_job *jobs, size_t n_jobs, void *stream) {
-    if (!jobs && n_jobs) return AFX_E_INVALID_ARG;
-    for (size_t i = 0; i < n_jobs; ++i) {
-        const int rc = check_job(jobs[i]);
-        if (rc != AFX_OK) return rc;
-    }
-    if (outputs_overlap(jobs, n_jobs)) return AFX_E_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    for (size_t i = 0; i < n_jobs; i += AFX_MAX_JOBS_PER_LAUNCH) {
-        const size_t k = std::min<size_t>(AFX_MAX_JOBS_PER_LAUNCH, n_jobs - i);
-        const int rc = launch(jobs + i, k, s);
-        if (rc != AFX_OK) return rc;
-    }
-    return AFX_OK;
+    const int rc = check_batch(jobs, n_jobs);
+    return rc != AFX_OK ? rc : decode_batch(jobs, n_jobs, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

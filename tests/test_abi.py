@@ -126,6 +126,42 @@ def test_decode_argument_errors_before_any_hip_call(L):
     assert L.afx_decode_layer_async(jobs, 3, None) == afx.AFX_E_INVALID_ARG  # job 2's blob is job 1's output
 
 
+
+def test_batch_overlap_check_matches_brute_force(L):
+    """Random batches of up to 40 jobs over a small address range: the
+    library rejects a batch exactly when some output shares a byte with
+    another output or with any blob. A batch that passes the check goes on to
+    the launch, which fails here for want of a GPU (never a device access:
+    the test is skipped where a GPU is present, since the addresses are
+    made up)."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("made-up device addresses must not reach a launch")
+    x, blob = c1_blob()
+    info = afx.afx_query(blob)
+    n, nb = int(info.n_elems), int(info.blob_bytes)
+    rng = np.random.default_rng(5)
+    base, unit = 1 << 40, 4096
+    seen = {True: 0, False: 0}
+    for trial in range(400):
+        k = int(rng.integers(2, 41))
+        span = int(rng.integers(4, 12)) * k  # address slots of `unit` bytes
+        blobs = [base + unit * int(rng.integers(0, span)) for _ in range(k)]
+        outs = [base + unit * int(rng.integers(0, span)) for _ in range(k)]
+        if trial % 2 == 0:  # disjoint outputs far from the blobs, or one planted overlap
+            outs = [base + (1 << 36) + i * 2 * (2 * n + unit) for i in range(k)]
+            if trial % 4 == 0:
+                outs[int(rng.integers(k))] = blobs[int(rng.integers(k))] + 16 * int(rng.integers(0, 4))
+        def hit(a0, a1, b0, b1):
+            return a0 < b1 and b0 < a1
+        want = any(hit(outs[i], outs[i] + 2 * n, outs[j], outs[j] + 2 * n) for i in range(k) for j in range(i))
+        want |= any(hit(outs[i], outs[i] + 2 * n, blobs[j], blobs[j] + nb) for i in range(k) for j in range(k))
+        jobs = afx.make_jobs([(info, b, o, 2 * n) for b, o in zip(blobs, outs)])
+        rc = L.afx_decode_layer_async(jobs, k, None)
+        assert (rc == afx.AFX_E_INVALID_ARG) == want, (trial, rc)
+        seen[want] += 1
+    assert min(seen.values()) > 80, seen
+
 # ---------------------------------------------------------------------------
 # The library's own encoder: its blobs must satisfy the oracle decoder and
 # its code must be as short as the oracle's optimum.
