@@ -170,15 +170,15 @@ struct GemmLds {
     LutScratch scratch;
 };
 
-// kTB: 32-token blocks per wave, so a workgroup multiplies each restored
-// slab with 128 kTB tokens. With two, only the A operands of the slab's
-// first 4 steps are fetched before the restore; each later step's are
-// fetched 4 steps ahead, during the matrix instructions, to fit the
-// registers. kTB = 0: one block of 32 tokens for the whole workgroup (m <=
-// 32), and the slab's 16 steps split over the waves (4 each), each wave
-// adding its partial sums into y, so that no wave multiplies alone while
-// the others wait.
-template <int kTB>
+// kB: 32-token blocks per wave; kWays: waves that share a token block, each
+// multiplying kSlabCols / 16 / kWays of the slab's 16-column steps (their
+// partial sums meet in LDS at the end of the tile), so that no wave
+// multiplies alone while the others wait at the barrier. A workgroup thus multiplies each restored slab with
+// 32 kB (4 / kWays) tokens: 32 (kWays 4), 64 (2), 128 (1) or 256 (kB 2).
+// With kB = 2, only the A operands of the slab's first 4 steps are fetched
+// before the restore; each later step's are fetched 4 steps ahead, during
+// the matrix instructions, to fit the registers.
+template <int kB, int kWays>
 __global__ __launch_bounds__(kGemmThreads, 2)
 void afx_gemm_kernel(const GemmBatch batch) {
     __shared__ __attribute__((aligned(16))) GemmLds lds;
@@ -198,9 +198,8 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t r0 = (tile % J.n_rtiles) * kTileRows;
     const uint32_t kbeg = (tile / J.n_rtiles) * kRangeCols;
     const uint32_t kend = min(J.cols, kbeg + kRangeCols);
-    constexpr bool kSplit = kTB == 0;
-    constexpr int kB = kSplit ? 1 : kTB;  // token blocks per wave
-    const uint32_t t0 = blockIdx.y * (kSplit ? 32 : kGemmWaves * 32 * kTB);
+    static_assert(kGemmWaves % kWays == 0 && (kSlabCols / 16) % kWays == 0, "waves share a token block's steps");
+    const uint32_t t0 = blockIdx.y * (32 * kB * (kGemmWaves / kWays));
     const uint32_t m = batch.m;
 
     // The code lengths and the first slabs' bit offsets are requested
@@ -215,7 +214,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     uint32_t *seg = stage + row * kSegRow;
     uint8_t *out_row = slab + row * kSlabStride;
     // Multiply: this lane's token (A row) in each of the wave's token blocks.
-    const uint32_t t_wave = kSplit ? t0 : t0 + wave * 32 * kTB;
+    const uint32_t t_wave = t0 + (wave / kWays) * 32 * kB;
     bool tok_ok[kB], blk_mul[kB];
     const uint16_t *xa_p[kB];
 #pragma unroll
@@ -243,11 +242,11 @@ void afx_gemm_kernel(const GemmBatch batch) {
     f32x16 acc[kB][2];
 #pragma unroll
     for (int tb = 0; tb < kB; ++tb) acc[tb][0] = acc[tb][1] = f32x16{};
-    // 16-column steps of a slab that this wave multiplies: all, or its 4
-    // (steps 4 wave .. 4 wave + 3) when split
-    constexpr uint32_t kSteps = kSplit ? kSlabCols / 16 / kGemmWaves : kSlabCols / 16;
-    const uint32_t ks0 = kSplit ? kSteps * wave : 0;
-    constexpr uint32_t kPre = kTB == 2 ? kSteps / 4 : kSteps;  // A steps fetched before the restore
+    // 16-column steps of a slab that this wave multiplies: all, or its share
+    // of the kWays waves that multiply its token blocks
+    constexpr uint32_t kSteps = kSlabCols / 16 / kWays;
+    const uint32_t ks0 = kSteps * (wave % kWays);
+    constexpr uint32_t kPre = kB == 2 ? kSteps / 4 : kSteps;  // A steps fetched before the restore
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
@@ -312,6 +311,31 @@ void afx_gemm_kernel(const GemmBatch batch) {
         bits_c = bits_n;
         bits_n = bits_nn;
         data_c = data_n;
+    }
+    if constexpr (kWays > 1) {
+        // The waves that share a token block add their partial sums in LDS
+        // (the slab's space, free after the last barrier), so that one wave
+        // per block adds into y: as many atomic adds as without the split.
+        static_assert(kB == 1 && kGemmWaves * 2 * 16 * kWave * 4 <= sizeof(GemmLds::slab), "partial sums fit the slab");
+        float *part = reinterpret_cast<float *>(slab) + wave * (2 * 16 * kWave);
+        if (wave_mul && wave % kWays != 0) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                part[v * kWave + lane] = acc[0][0][v];
+                part[(16 + v) * kWave + lane] = acc[0][1][v];
+            }
+        }
+        __syncthreads();
+        if (wave % kWays != 0) return;
+#pragma unroll
+        for (int w = 1; w < kWays; ++w) {
+            const float *pw = part + w * (2 * 16 * kWave);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                acc[0][0][v] += pw[v * kWave + lane];
+                acc[0][1][v] += pw[(16 + v) * kWave + lane];
+            }
+        }
     }
     if (!wave_mul) return;
     const uint32_t col = r0 + ((uint32_t)lane & 31);
@@ -380,15 +404,16 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     }
     if (tiles == 0) return AFX_OK;
     if (tiles >= (1ull << 31)) return AFX_E_UNSUPPORTED;
-    // one block of 32 tokens shared by the waves while it covers m; one per
-    // wave while 128 cover it; else two per wave
-    const uint32_t tb = m <= 32 ? 0 : m <= kGemmWaves * 32 ? 1 : 2;
-    const uint32_t per_wg = tb == 0 ? 32 : kGemmWaves * 32 * tb;
+    // one block of 32 tokens shared by the four waves while it covers m, two
+    // blocks shared by two waves each while they do, one block per wave while
+    // 128 tokens cover m, else two per wave
+    const uint32_t per_wg = m <= 32 ? 32 : m <= 64 ? 64 : m <= kGemmWaves * 32 ? kGemmWaves * 32 : kGemmWaves * 64;
     const uint32_t tok_blocks = (m + per_wg - 1) / per_wg;
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
-    const void *fn = tb == 0   ? reinterpret_cast<const void *>(&afx_gemm_kernel<0>)
-                     : tb == 1 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1>)
-                               : reinterpret_cast<const void *>(&afx_gemm_kernel<2>);
+    const void *fn = m <= 32   ? reinterpret_cast<const void *>(&afx_gemm_kernel<1, 4>)
+                     : m <= 64 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1, 2>)
+                     : m <= kGemmWaves * 32 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1, 1>)
+                                            : reinterpret_cast<const void *>(&afx_gemm_kernel<2, 1>);
     return hipLaunchKernel(fn, dim3((unsigned)tiles, tok_blocks), dim3(kGemmThreads), args, 0, stream) == hipSuccess
                ? AFX_OK
                : AFX_E_HIP;
