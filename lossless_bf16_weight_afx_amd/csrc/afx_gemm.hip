@@ -163,9 +163,12 @@ __device__ inline SlabData slab_data(const TensorDesc &T, uint64_t e_seg, uint32
 
 // The workgroup's LDS as one object, the decode table first: at LDS address
 // 0 a table read needs no base added to its index.
+// Row r of the tile has one kSlabStride-byte slice: it holds the row's
+// staged code words while the row decodes, then its restored values (the
+// same lanes do both, so a wave-level order between them suffices).
+static_assert(kSegRow * 4 <= kSlabStride, "a row's staged words fit its slab row");
 struct GemmLds {
     uint16_t lut[kLutEntries];                    // 8 KB
-    uint32_t stage[kTileRows * kSegRow];          // 27 KB
     uint8_t slab[kTileRows * kSlabStride];        // 33 KB
     LutScratch scratch;
 };
@@ -179,11 +182,10 @@ struct GemmLds {
 // before the restore; each later step's are fetched 4 steps ahead, during
 // the matrix instructions, to fit the registers.
 template <int kB, int kWays>
-__global__ __launch_bounds__(kGemmThreads, 2)
+__global__ __launch_bounds__(kGemmThreads, kWays > 1 ? 3 : 2)
 void afx_gemm_kernel(const GemmBatch batch) {
     __shared__ __attribute__((aligned(16))) GemmLds lds;
     uint16_t *lut = lds.lut;
-    uint32_t *stage = lds.stage;
     uint8_t *slab = lds.slab;
     LutScratch &scratch = lds.scratch;
 
@@ -211,7 +213,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t q4 = (uint32_t)lane & 3;
     const uint32_t row = wave * kRowsPerWave + ((uint32_t)lane >> 2);  // tile-local
     const uint64_t row_e = (uint64_t)(r0 + row) * J.cols;              // element of W[r0 + row, 0]
-    uint32_t *seg = stage + row * kSegRow;
+    uint32_t *seg = reinterpret_cast<uint32_t *>(slab + row * kSlabStride);
     uint8_t *out_row = slab + row * kSlabStride;
     // Multiply: this lane's token (A row) in each of the wave's token blocks.
     const uint32_t t_wave = t0 + (wave / kWays) * 32 * kB;
@@ -246,7 +248,9 @@ void afx_gemm_kernel(const GemmBatch batch) {
     // of the kWays waves that multiply its token blocks
     constexpr uint32_t kSteps = kSlabCols / 16 / kWays;
     const uint32_t ks0 = kSteps * (wave % kWays);
-    constexpr uint32_t kPre = kB == 2 ? kSteps / 4 : kSteps;  // A steps fetched before the restore
+    // A steps fetched before the restore (the rest a few steps ahead during
+    // the matrix instructions, where the registers are short)
+    constexpr uint32_t kPre = kB == 2 ? kSteps / 4 : kWays == 2 ? kSteps / 2 : kSteps;
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
@@ -270,6 +274,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
         uint32_t ex1[8], ex2[8];
         decode_groups(seg, seg_chain_r0(bit1(bits_c), data_c.wa), seg_chain_r0(bit2(bits_c), data_c.wa), lut, ex1,
                       ex2);
+        wave_sync();  // the row's staged words have been read: its slab row may be written
         // Join and put both groups into the slab.
         const uint32_t b1[8] = {data_c.s1a.x, data_c.s1a.y, data_c.s1a.z, data_c.s1a.w,
                                 data_c.s1b.x, data_c.s1b.y, data_c.s1b.z, data_c.s1b.w};
