@@ -182,7 +182,7 @@ struct GemmLds {
 // before the restore; each later step's are fetched 4 steps ahead, during
 // the matrix instructions, to fit the registers.
 template <int kB, int kWays>
-__global__ __launch_bounds__(kGemmThreads, kWays > 1 ? 3 : 2)
+__global__ __launch_bounds__(kGemmThreads, kB == 1 ? 3 : 2)
 void afx_gemm_kernel(const GemmBatch batch) {
     __shared__ __attribute__((aligned(16))) GemmLds lds;
     uint16_t *lut = lds.lut;
@@ -250,7 +250,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t ks0 = kSteps * (wave % kWays);
     // A steps fetched before the restore (the rest a few steps ahead during
     // the matrix instructions, where the registers are short)
-    constexpr uint32_t kPre = kB == 2 ? kSteps / 4 : kWays == 2 ? kSteps / 2 : kSteps;
+    constexpr uint32_t kPre = kB == 2 || kWays == 1 ? kSteps / 4 : kWays == 2 ? kSteps / 2 : kSteps;
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
