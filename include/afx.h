@@ -127,7 +127,8 @@ int afx_decode_tensor(const afx_info *info, const void *blob_dev, void *out_dev,
  * the stream or events recorded on it. All jobs are checked before anything
  * is enqueued. Errors: as afx_decode_tensor, but only enqueue-time HIP errors
  * are reported; AFX_E_HOST_MEMORY when the host memory for the overlap check
- * cannot be had. */
+ * of a batch of more than 1024 jobs cannot be had (up to 1024 it allocates
+ * nothing). */
 int afx_decode_layer_async(const afx_job *jobs, size_t n_jobs, void *stream);
 
 /* afx_status_str: a static description of a status code. */

@@ -249,30 +249,40 @@ int check_job(const afx_job &j) {
 // must be disjoint, and each blob must miss the output that starts last at
 // or below its end (the outputs being disjoint, that is the only one that
 // can reach into it). O(n log n): a whole model's tensors in one call.
-// Returns -1 when host memory for the sort cannot be had.
+// Returns -1 when host memory for the sort cannot be had (more than
+// kStackRanges jobs only).
 int outputs_overlap(const afx_job *jobs, size_t n) {
     struct Range {
         uintptr_t lo, hi;  // [lo, hi)
     };
-    std::vector<Range> outs;
-    try {
-        outs.reserve(n);
-    } catch (...) {
-        return -1;
+    // the outputs' ranges: on the stack for up to kStackRanges jobs (a whole
+    // model's tensors), on the heap beyond
+    constexpr size_t kStackRanges = 1024;
+    Range local[kStackRanges];
+    std::vector<Range> heap;
+    Range *outs = local;
+    if (n > kStackRanges) {
+        try {
+            heap.resize(n);
+        } catch (...) {
+            return -1;
+        }
+        outs = heap.data();
     }
+    size_t k = 0;
     for (size_t i = 0; i < n; ++i) {
         const uintptr_t o = reinterpret_cast<uintptr_t>(jobs[i].out_dev);
-        if (jobs[i].info->decoded_bytes) outs.push_back(Range{o, o + jobs[i].info->decoded_bytes});
+        if (jobs[i].info->decoded_bytes) outs[k++] = Range{o, o + jobs[i].info->decoded_bytes};
     }
-    std::sort(outs.begin(), outs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
-    for (size_t i = 1; i < outs.size(); ++i)
+    std::sort(outs, outs + k, [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < k; ++i)
         if (outs[i].lo < outs[i - 1].hi) return 1;
     for (size_t i = 0; i < n; ++i) {
         if (!jobs[i].info->n_elems) continue;
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(jobs[i].blob_dev), b1 = b0 + jobs[i].info->blob_bytes;
         // the last output starting below the blob's end
-        auto it = std::lower_bound(outs.begin(), outs.end(), b1, [](const Range &r, uintptr_t v) { return r.lo < v; });
-        if (it != outs.begin() && std::prev(it)->hi > b0) return 1;
+        const Range *it = std::lower_bound(outs, outs + k, b1, [](const Range &r, uintptr_t v) { return r.lo < v; });
+        if (it != outs && (it - 1)->hi > b0) return 1;
     }
     return 0;
 }

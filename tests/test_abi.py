@@ -161,6 +161,15 @@ def test_batch_overlap_check_matches_brute_force(L):
         assert (rc == afx.AFX_E_INVALID_ARG) == want, (trial, rc)
         seen[want] += 1
     assert min(seen.values()) > 80, seen
+    # past 1024 jobs the ranges go to the heap: same answers
+    k = 1100
+    blobs = [base + i * 2 * (nb + unit) for i in range(k)]
+    outs = [base + (1 << 36) + i * 2 * (2 * n + unit) for i in range(k)]
+    jobs = afx.make_jobs([(info, b, o, 2 * n) for b, o in zip(blobs, outs)])
+    assert L.afx_decode_layer_async(jobs, k, None) != afx.AFX_E_INVALID_ARG
+    outs[k - 1] = blobs[3] + 16
+    jobs = afx.make_jobs([(info, b, o, 2 * n) for b, o in zip(blobs, outs)])
+    assert L.afx_decode_layer_async(jobs, k, None) == afx.AFX_E_INVALID_ARG
 
 # ---------------------------------------------------------------------------
 # The library's own encoder: its blobs must satisfy the oracle decoder and
