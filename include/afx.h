@@ -3,10 +3,11 @@
  *
  * The operation. "Why Weight Offloading Slows Inference" (section "Three
  * steps for each weight", Eq. (1)) puts an unpack step, t_unpack, between
- * reading a stored weight and using it; section "Lossless compression" stores
- * BF16 weights with shorter codes for common exponent values (Huffman's
- * minimum-redundancy code, that page's reference [2]) and restores the exact
- * released bits before compute. This library performs that restore on an
+ * reading a stored weight and using it; section "Lossless compression"
+ * entropy-codes the BF16 exponent field without loss (a minimum-redundancy
+ * prefix code, that page's reference [2]), so that each weight's original
+ * 16 bits must be reconstructed before it is used. This library performs that
+ * reconstruction on an
  * AMD Instinct MI355X (gfx950), after the compressed bytes have been copied
  * to device memory, and writes the BF16 bit patterns into a caller buffer.
  *
@@ -158,9 +159,9 @@ int afx_encode(const uint16_t *x, uint64_t n, uint32_t ndim, const uint64_t *sha
                int threads);
 
 /* ---- The restore fused into its consumer. "Why Weight Offloading Slows
- * Inference" (section "Lossless compression") restores the released bits
- * before computation; for a matrix-vector product the restored matrix need
- * not reach HBM at all. */
+ * Inference" (section "Lossless compression") reconstructs a weight's bits
+ * ahead of the computation that uses it; when that computation is a product
+ * on the GPU, the reconstructed matrix need not reach HBM at all. */
 
 /* afx_restore_gemv_async: y += W x, where W is the tensor of the device blob
  * (info from afx_query on a host copy), taken as row-major [rows, cols]

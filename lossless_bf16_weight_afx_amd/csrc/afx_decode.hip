@@ -2,10 +2,10 @@
 //
 // "Why Weight Offloading Slows Inference" (section "Three steps for each
 // weight", Eq. (1)) names the unpack time t_unpack that every compressed
-// weight pays before use; section "Lossless compression" codes the BF16
-// exponent with shorter codes for common values and restores the released
-// bits before compute. Here that unpack runs on the GPU after the compressed
-// bytes reach device memory.
+// weight pays before use; section "Lossless compression" entropy-codes the
+// BF16 exponent field, so the unpack reconstructs each weight's exact bits.
+// Here that unpack runs on the GPU after the compressed bytes reach device
+// memory.
 //
 // Work decomposition (one launch per batch of up to 32 tensors):
 //   * one workgroup of 16 wave64s fills a CU (4 waves per SIMD). The grid

@@ -5,8 +5,8 @@
 //
 // A tensor's exponent codes come in chunks of 4096 elements, each starting at
 // a recorded bit base, with the start of every 32-element group recorded as a
-// gap from its chunk's base; "Why Weight Offloading Slows Inference" (section
-// "Lossless compression") gives the exponent the shorter codes.
+// gap from its chunk's base (the exponent field is the coded part: "Why
+// Weight Offloading Slows Inference", section "Lossless compression").
 #pragma once
 
 #include <hip/hip_runtime.h>

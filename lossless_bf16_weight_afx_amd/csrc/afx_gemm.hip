@@ -2,8 +2,8 @@
 // (gfx950): Y += X W^T for a weight matrix W held only in its coded form.
 //
 // "Why Weight Offloading Slows Inference" (section "Lossless compression")
-// restores the released bits of a compressed weight before computation. For a
-// product over many tokens at once (a prompt), restoring W into HBM first
+// reconstructs a coded weight's bits ahead of the computation that uses it.
+// For a product over many tokens at once (a prompt), restoring W into HBM first
 // writes and rereads 2 bytes per weight; here tiles of W are restored into
 // LDS and consumed there by MFMA, and only the coded matrix is read from HBM.
 //

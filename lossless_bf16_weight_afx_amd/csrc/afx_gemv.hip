@@ -2,7 +2,7 @@
 // weight matrix W held only in its coded form.
 //
 // "Why Weight Offloading Slows Inference" (section "Lossless compression")
-// restores the released bits of a compressed weight before computation.
+// reconstructs a coded weight's bits ahead of the computation that uses it.
 // Restoring into HBM and then multiplying writes the BF16 matrix (2 bytes per
 // value) and reads it back; for the matrix-vector products of token-by-token
 // generation, which read every weight once per token, that traffic is the

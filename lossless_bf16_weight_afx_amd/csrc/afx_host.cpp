@@ -4,7 +4,7 @@
 // The coding follows "Why Weight Offloading Slows Inference", section
 // "Lossless compression": the BF16 exponent field gets a per-tensor
 // minimum-redundancy code (Huffman, that page's reference [2]), the other
-// eight bits stay raw, and decoding restores the exact released bits. The
+// eight bits stay raw, and decoding gives back every value's exact bits. The
 // code lengths are limited to 12 bits so that one 4096-entry table decodes
 // any code word.
 #include "afx_internal.h"

@@ -12,9 +12,9 @@
 //
 // The format: a tensor's exponent codes form one MSB-first bit stream of u32
 // words; each 4096-element chunk starts at a recorded u64 bit base, and each
-// 32-element group at a u16 gap after its chunk's base ("Why Weight
-// Offloading Slows Inference", section "Lossless compression", gives the
-// exponent field the shorter codes).
+// 32-element group at a u16 gap after its chunk's base (the exponent field is
+// the coded part: "Why Weight Offloading Slows Inference", section "Lossless
+// compression").
 #pragma once
 
 #include <cstdint>

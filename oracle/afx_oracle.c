@@ -6,11 +6,11 @@
  * code, header, table or constant generator with it.
  *
  * What it computes. "Why Weight Offloading Slows Inference" (section
- * "Lossless compression: fewer bytes to read, more work to unpack") stores
- * BF16 weights without loss by giving common BF16 exponent values shorter
- * codes, the minimum-redundancy code of Huffman (1952, that page's reference
- * [2]), and restores the released bits before compute. The pages fix nothing
- * else, so this oracle takes these readings:
+ * "Lossless compression") codes the BF16 exponent field with Huffman's
+ * minimum-redundancy prefix code (1952, that page's reference [2]): frequent
+ * exponents cost fewer bits, nothing is lost, and decoding gives back every
+ * weight's original 16 bits. The pages fix nothing else, so this oracle
+ * takes these readings:
  *
  *   - BF16 layout: bit 15 sign, bits 14..7 biased exponent, bits 6..0
  *     mantissa. The 8-bit exponent field is the coded symbol (all 256 values,

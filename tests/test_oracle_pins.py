@@ -34,8 +34,8 @@ def cost(freq, lens):
 
 
 # ---------------------------------------------------------------------------
-# P-RT: decode(encode(x)) == x bit for bit ("restores the released bits",
-# page 2, section "Lossless compression").
+# P-RT: decode(encode(x)) == x bit for bit (the coding is lossless: page 2,
+# section "Lossless compression").
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 128, 4095, 4096, 4097, 5120, 3 * 4096 + 17])
 def test_roundtrip_sizes(n):
