@@ -58,6 +58,9 @@ def small_ints(rng, shape, lo, hi):
     (192, 2816, 130),   # two column ranges (2560 + 256), two token blocks
     (64, 17408, 64),    # down_proj-shaped rows: seven column ranges
     (128, 512, 300),    # two token blocks per wave, two token tiles, the last one partial
+    (128, 2816, 48),    # two waves share each token block (partial second block), two column ranges
+    (64, 1024, 100),    # one block per wave, the fourth partial
+    (64, 768, 20),      # four waves share one partial token block
 ])
 def test_integer_data_exact(rows, cols, m):
     say(f"[gpu] case gemm integers {rows}x{cols} m={m}")
