@@ -376,7 +376,8 @@ def bench_gemv(args, threads: int) -> int:
         raise SystemExit("--workload gemv takes --m 1, 2 or 4")
     if m < 1:
         raise SystemExit("--m must be at least 1")
-    kernel = "afx_gemm_kernel" if gemm else "afx_gemv_kernel"
+    # (the MFMA entry point runs the matrix-vector kernel for 1, 2 or 4 tokens)
+    kernel = "afx_gemm_kernel" if gemm and m not in (1, 2, 4) else "afx_gemv_kernel"
     launch = afx.afx_restore_gemm_batch_async if gemm else afx.afx_restore_gemv_batch_async
     tol = 1.0  # the summation bound (for the matrix instruction, as measured by test_one_matrix_instruction_rounding)
     specs = [sp for sp in synth.decoder_layer(0) if len(sp.shape) == 2]

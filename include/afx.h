@@ -206,7 +206,9 @@ int afx_restore_gemv_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32
  * [rows, cols] (rows * cols == n_elems), x is BF16 [m, cols] and y FP32
  * [m, rows], both row-major in device memory; any m >= 1. 64-row tiles of W
  * are restored into LDS 256 columns at a time and multiplied there with
- * BF16 matrix instructions (FP32 accumulation); tiles over different column
+ * BF16 matrix instructions (FP32 accumulation); for m = 1, 2 or 4 the call
+ * runs afx_restore_gemv_async's kernel instead, which is faster for so few
+ * tokens (the same y within the same bound). Tiles over different column
  * ranges of the same rows add their partial sums into y with atomic adds,
  * so their order (and the last bits) may differ between calls. The caller
  * owns y and its initial contents. Enqueued on stream; returns without

@@ -438,6 +438,9 @@ int afx_restore_gemm_batch_async(const afx_gemv_job *jobs, size_t n_jobs, uint32
         if (rc != AFX_OK) return rc;
     }
     if (fused_outputs_overlap_inputs(jobs, n_jobs, m)) return AFX_E_INVALID_ARG;
+    // For 1, 2 or 4 tokens the matrix-vector kernel computes the same y on
+    // the vector ALUs faster (it accepts every job this one does).
+    if (m == 1 || m == 2 || m == 4) return afx_restore_gemv_batch_async(jobs, n_jobs, m, stream);
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (size_t i = 0; i < n_jobs; i += AFX_MAX_GEMV_JOBS_PER_LAUNCH) {
         const size_t k = std::min<size_t>(AFX_MAX_GEMV_JOBS_PER_LAUNCH, n_jobs - i);
