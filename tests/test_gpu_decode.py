@@ -249,6 +249,56 @@ def test_many_small_tensors_split_over_launches():
         assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
 
 
+def restore_batch_exact(xs, name):
+    """Encode xs with the library, restore them with one batch call into
+    outputs followed by guard words, and compare every output exactly."""
+    blobs = [afx.afx_encode(x, threads=8) for x in xs]
+    infos = [afx.afx_query(b) for b in blobs]
+    devs = [afx.to_device(b) for b in blobs]
+    outs = [torch.full((x.size + 64,), 0x5A5A, dtype=torch.int16, device="cuda") for x in xs]
+    say(f"[gpu] case {name}: {len(xs)} tensors, chunks {[int(i.n_chunks) for i in infos]}")
+    afx.afx_decode_layer_async([(i, d.data_ptr(), o.data_ptr(), 2 * x.size)
+                                for i, d, o, x in zip(infos, devs, outs, xs)], 0)
+    torch.cuda.synchronize()
+    for k, (x, o) in enumerate(zip(xs, outs)):
+        y = o.cpu().numpy().view(np.uint16)
+        assert np.all(y[x.size:] == 0x5A5A), f"{name}: tensor {k} wrote past its output"
+        assert np.array_equal(y[:x.size], x), f"{name}: tensor {k} differs"
+
+
+def test_twelve_mid_size_tensors_one_launch():
+    """Twelve tensors of 256-700 chunks with ragged ends, normal and
+    heavy-tailed values, in one launch: the grid is split twelve ways, each
+    workgroup restoring one tensor's share with that tensor's table."""
+    rng = np.random.default_rng(12)
+    xs = [synth.generate(synth.TensorSpec(f"w{i}", (int(rng.integers(256, 700)) * 4096 - int(rng.integers(0, 4000)),),
+                                          "t4" if i % 3 == 0 else "normal", 700 + i))
+          for i in range(12)]
+    restore_batch_exact(xs, "12 mid-size tensors")
+
+
+def test_workgroups_with_fewer_chunks_than_waves():
+    """Three tensors (1000, 600 and 300 chunks) split over the grid leave
+    each workgroup about eight chunks, fewer than its 16 waves: waves without
+    a chunk of their own skip the tensor, the others restore it."""
+    xs = [synth.generate(synth.TensorSpec(f"f{i}", (c * 4096 + 100 * i,), "normal", 800 + i))
+          for i, c in enumerate((1000, 600, 300))]
+    restore_batch_exact(xs, "few chunks per workgroup")
+
+
+def test_full_launch_of_mixed_tensors():
+    """32 tensors in one launch (the most one launch holds): eight of about
+    300 chunks and 24 small ones down to one element, in a random order, with
+    ragged ends; the small ones share workgroups."""
+    rng = np.random.default_rng(32)
+    xs = [synth.generate(synth.TensorSpec(f"m{i}", (300 * 4096 + int(rng.integers(0, 4096)),), "normal", 900 + i))
+          for i in range(8)]
+    xs += [synth.generate(synth.TensorSpec(f"s{i}", (int(rng.integers(1, 20000)),), "normal", 950 + i))
+           for i in range(24)]
+    order = rng.permutation(len(xs))
+    restore_batch_exact([xs[i] for i in order], "32 mixed tensors")
+
+
 def test_embedding_full_size():
     """151936 x 5120 heavy-tailed tensor, bit-exact in full."""
     spec = synth.embedding()[0]
