@@ -142,6 +142,9 @@ def main() -> int:
                     help="directory for the model store file (--workload disk)")
     ap.add_argument("--keep-store", action="store_true", help="keep the store file afterwards (--workload disk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-workgroups", type=int, default=0,
+                    help="restore on at most this many workgroups (CUs) per launch, through "
+                         "afx_decode_layer_grid_async (--workload layer, tensor-1024, q_proj or embedding)")
     ap.add_argument("--copies", type=int, default=0,
                     help="rotate over this many blob/output copies (default: enough for about 4 GB between "
                          "two touches of one copy)")
@@ -162,6 +165,9 @@ def main() -> int:
     afx.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     threads = cpu_share()
+    if args.max_workgroups and args.workload not in ("layer", "tensor-1024", "q_proj", "embedding"):
+        print("--max-workgroups applies to --workload layer, tensor-1024, q_proj or embedding", file=sys.stderr)
+        return 2
     if args.workload == "model":
         return bench_model(args, threads)
     if args.workload == "disk":
@@ -173,6 +179,14 @@ def main() -> int:
     if args.workload == "token":
         return bench_token(args, threads)
     workload, specs = workload_specs(args.workload)
+    if args.max_workgroups < 0:
+        print("--max-workgroups must be positive", file=sys.stderr)
+        return 2
+    if args.max_workgroups:
+        def enqueue(jobs, s):
+            afx.afx_decode_layer_grid_async(jobs, args.max_workgroups, s)
+    else:
+        enqueue = afx.afx_decode_layer_async
 
     # ---- inputs: generate, encode with the library's encoder, move to HBM
     t0 = time.time()
@@ -202,7 +216,7 @@ def main() -> int:
 
     # ---- correctness pass (separate from timing): every copy, bit-exact
     for c in range(copies):
-        afx.afx_decode_layer_async(jobsets[c], sp)
+        enqueue(jobsets[c], sp)
     torch.cuda.synchronize()
     exact = True
     for t, x in enumerate(xs):
@@ -218,7 +232,7 @@ def main() -> int:
     t_warm, w = time.time(), 0
     while True:  # warm-up: at least W steps and about half a second of work
         for _ in range(max(1, args.warmup)):
-            afx.afx_decode_layer_async(jobsets[w % copies], sp)
+            enqueue(jobsets[w % copies], sp)
             w += 1
         torch.cuda.synchronize()
         if time.time() - t_warm > 0.5:
@@ -228,7 +242,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t_all0.record(stream)
     for k in range(args.steps):
-        afx.afx_decode_layer_async(jobsets[(w + k) % copies], sp)
+        enqueue(jobsets[(w + k) % copies], sp)
     t_all1.record(stream)
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
@@ -240,12 +254,12 @@ def main() -> int:
     # its code words still sit in the memory-side cache), timed apart from
     # the cold rotation above and reported beside it, labelled
     for _ in range(max(1, args.warmup)):
-        afx.afx_decode_layer_async(jobsets[0], sp)
+        enqueue(jobsets[0], sp)
     h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     h0.record(stream)
     for _ in range(args.steps):
-        afx.afx_decode_layer_async(jobsets[0], sp)
+        enqueue(jobsets[0], sp)
     h1.record(stream)
     torch.cuda.synchronize()
     hot_ms = h0.elapsed_time(h1) / args.steps
@@ -257,7 +271,8 @@ def main() -> int:
 
     achieved = traffic_pass / (launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profile_traffic(workload),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None if args.max_workgroups else profile_traffic(workload),
                 "algorithmic_bytes_per_launch": traffic_pass, "kernel": KERNEL_NAME,
                 "kernel_ms": round(launch_ms, 5), "copy_ceiling_GBps": round(copy_gbps, 1),
                 "calib_copy_bytes_each_way": copy_each_way}
@@ -304,7 +319,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "u32", "data": "synthetic",
         "config": {"workload": workload, "tensors": len(specs), "values": n_total, "restored_bytes": restored,
                    "blob_bytes": blob_total, "ratio": round(blob_total / restored, 4), "copies": copies,
-                   "encoder": "libafx afx_encode"},
+                   "encoder": "libafx afx_encode",
+                   **({"max_workgroups": args.max_workgroups} if args.max_workgroups else {})},
         "bit_exact": bool(exact), "roofline": roofline, "hot_one_copy": hot, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -132,6 +132,17 @@ int afx_decode_tensor(const afx_info *info, const void *blob_dev, void *out_dev,
  * nothing). */
 int afx_decode_layer_async(const afx_job *jobs, size_t n_jobs, void *stream);
 
+/* afx_decode_layer_grid_async: afx_decode_layer_async on at most
+ * max_workgroups workgroups per launch (one workgroup per CU at most, so
+ * this many CUs at most; a larger value is the whole device, as in
+ * afx_decode_layer_async). For a caller that restores the next unit while
+ * its computation runs on the same GPU ("Why Weight Offloading Slows
+ * Inference", section "Loading during computation"): the restore then
+ * leaves the other CUs to that computation. Outputs are the same bits for
+ * every max_workgroups. Errors: as afx_decode_layer_async;
+ * AFX_E_INVALID_ARG when max_workgroups is 0. */
+int afx_decode_layer_grid_async(const afx_job *jobs, size_t n_jobs, uint32_t max_workgroups, void *stream);
+
 /* afx_status_str: a static description of a status code. */
 const char *afx_status_str(int status);
 

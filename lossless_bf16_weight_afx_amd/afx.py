@@ -28,7 +28,8 @@ MAX_JOBS_PER_LAUNCH = 32
 AFX_READ_DIRECT = 1
 
 # Every symbol include/afx.h declares.
-EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_status_str",
+EXPORTS = ("afx_query", "afx_decode_tensor", "afx_decode_layer_async", "afx_decode_layer_grid_async",
+           "afx_status_str",
            "afx_encode_plan", "afx_encode", "afx_file_read", "afx_decode_host",
            "afx_restore_gemv_async", "afx_restore_gemv_batch_async", "afx_restore_gemm_async",
            "afx_restore_gemm_batch_async")
@@ -106,6 +107,9 @@ def lib() -> ctypes.CDLL:
         L.afx_decode_tensor.restype = ctypes.c_int
         L.afx_decode_layer_async.argtypes = [ctypes.POINTER(afx_job), ctypes.c_size_t, ctypes.c_void_p]
         L.afx_decode_layer_async.restype = ctypes.c_int
+        L.afx_decode_layer_grid_async.argtypes = [ctypes.POINTER(afx_job), ctypes.c_size_t, ctypes.c_uint32,
+                                                  ctypes.c_void_p]
+        L.afx_decode_layer_grid_async.restype = ctypes.c_int
         L.afx_status_str.argtypes = [ctypes.c_int]
         L.afx_status_str.restype = ctypes.c_char_p
         L.afx_encode_plan.argtypes = [u16p, ctypes.c_uint64, ctypes.c_int, u8p, u64p, u64p]
@@ -204,6 +208,13 @@ def afx_decode_layer_async(jobs, stream: int = 0) -> None:
     """
     arr = jobs if isinstance(jobs, ctypes.Array) else make_jobs(jobs)
     _check(lib().afx_decode_layer_async(arr, len(arr), ctypes.c_void_p(stream)), "afx_decode_layer_async")
+
+
+def afx_decode_layer_grid_async(jobs, max_workgroups: int, stream: int = 0) -> None:
+    """afx_decode_layer_async on at most ``max_workgroups`` workgroups (CUs)."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else make_jobs(jobs)
+    _check(lib().afx_decode_layer_grid_async(arr, len(arr), ctypes.c_uint32(max_workgroups), ctypes.c_void_p(stream)),
+           "afx_decode_layer_grid_async")
 
 
 def afx_encode_plan(x: np.ndarray, threads: int = 0):

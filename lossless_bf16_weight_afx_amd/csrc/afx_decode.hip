@@ -9,8 +9,8 @@
 //
 // Work decomposition (one launch per batch of up to 32 tensors):
 //   * one workgroup of 16 wave64s fills a CU (4 waves per SIMD). The grid
-//     is split among the batch's tensors in proportion to their chunk
-//     (4096-element) counts, so a workgroup serves about one tensor; within
+//     is split among the batch's tensors by their chunk (4096-element)
+//     counts (afx_split.h), so a workgroup serves about one tensor; within
 //     a tensor the chunks go round its workgroups, so that all of them move
 //     through each array together, in one narrow band;
 //   * the waves of a workgroup claim its chunks one at a time from a counter
@@ -39,6 +39,7 @@
 #include <vector>
 
 #include "afx_device.h"
+#include "afx_split.h"
 
 namespace afx {
 namespace {
@@ -306,12 +307,14 @@ TensorDesc describe(const afx_job &j) {
     return d;
 }
 
-// Enqueue one launch for up to AFX_MAX_JOBS_PER_LAUNCH already-checked jobs.
-int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
+// Enqueue one launch for up to AFX_MAX_JOBS_PER_LAUNCH already-checked jobs,
+// on at most cap workgroups (cap >= 1).
+int launch(const afx_job *jobs, size_t n_jobs, uint32_t cap, hipStream_t stream) {
     Batch batch;
     batch.n_tensors = 0;
-    uint64_t total = 0;
-    uint64_t first[AFX_MAX_JOBS_PER_LAUNCH];
+    uint64_t chunks[AFX_MAX_JOBS_PER_LAUNCH];
+    uint32_t lo[AFX_MAX_JOBS_PER_LAUNCH], hi[AFX_MAX_JOBS_PER_LAUNCH];
+    uint32_t n_big = 0;
     // Tensors of fewer chunks than a workgroup has waves (a layer's norm
     // vectors) go last: together they are then a sliver of the grid's last
     // share, served by a workgroup of their own (each tensor a workgroup
@@ -321,30 +324,20 @@ int launch(const afx_job *jobs, size_t n_jobs, hipStream_t stream) {
         for (size_t i = 0; i < n_jobs; ++i) {
             const uint64_t nc = jobs[i].info->n_chunks;
             if (nc == 0 || (pass == 0) != (nc >= kWavesPerBlock)) continue;
-            first[batch.n_tensors] = total;
+            chunks[batch.n_tensors] = nc;
             batch.t[batch.n_tensors++] = describe(jobs[i]);
-            total += nc;
+            n_big += pass == 0 ? 1u : 0u;
         }
     }
-    if (total == 0) return AFX_OK;
+    if (batch.n_tensors == 0) return AFX_OK;
     int max_blocks = 0;
     int rc = max_blocks_for_current_device(&max_blocks);
     if (rc != AFX_OK) return rc;
-    // Every workgroup should get the same number of chunks, or the launch
-    // ends with part of the grid idle: with at most max_blocks workgroups each
-    // takes ceil(total / max_blocks) chunks; use just enough workgroups.
-    const uint64_t per_block = (total + max_blocks - 1) / max_blocks;
-    const uint64_t want = (total + per_block - 1) / per_block;
-    const uint64_t grid = std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)max_blocks));
-    // Split the grid among the tensors in proportion to their chunk counts;
-    // a tensor too small for a workgroup of its own is served by the
-    // workgroup at its position (which may serve a neighbour too).
+    max_blocks = (int)std::min<uint64_t>((uint64_t)max_blocks, cap);
+    const uint32_t grid = split_grid(chunks, batch.n_tensors, n_big, (uint32_t)max_blocks, lo, hi);
     for (uint32_t t = 0; t < batch.n_tensors; ++t) {
-        const uint64_t lo = grid * first[t] / total;
-        uint64_t hi = grid * (first[t] + batch.t[t].n_chunks) / total;
-        if (hi <= lo) hi = lo + 1;
-        batch.t[t].blk_lo = (uint32_t)lo;
-        batch.t[t].blk_hi = (uint32_t)hi;
+        batch.t[t].blk_lo = lo[t];
+        batch.t[t].blk_hi = hi[t];
     }
     // hipLaunchKernel reports this launch's own status (an error left pending
     // by an earlier, unrelated HIP call is not mistaken for it)
@@ -368,10 +361,10 @@ int check_batch(const afx_job *jobs, size_t n_jobs) {
 }
 
 // The launches of a checked batch call.
-int decode_batch(const afx_job *jobs, size_t n_jobs, hipStream_t s) {
+int decode_batch(const afx_job *jobs, size_t n_jobs, uint32_t cap, hipStream_t s) {
     for (size_t i = 0; i < n_jobs; i += AFX_MAX_JOBS_PER_LAUNCH) {
         const size_t k = std::min<size_t>(AFX_MAX_JOBS_PER_LAUNCH, n_jobs - i);
-        const int rc = launch(jobs + i, k, s);
+        const int rc = launch(jobs + i, k, cap, s);
         if (rc != AFX_OK) return rc;
     }
     return AFX_OK;
@@ -389,14 +382,20 @@ int afx_decode_tensor(const afx_info *info, const void *blob_dev, void *out_dev,
     int rc = check_job(job);
     if (rc != AFX_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = launch(&job, 1, s);
+    rc = launch(&job, 1, UINT32_MAX, s);
     if (rc != AFX_OK) return rc;
     return hipStreamSynchronize(s) == hipSuccess ? AFX_OK : AFX_E_HIP;
 }
 
 int afx_decode_layer_async(const afx_job *jobs, size_t n_jobs, void *stream) {
     const int rc = check_batch(jobs, n_jobs);
-    return rc != AFX_OK ? rc : decode_batch(jobs, n_jobs, static_cast<hipStream_t>(stream));
+    return rc != AFX_OK ? rc : decode_batch(jobs, n_jobs, UINT32_MAX, static_cast<hipStream_t>(stream));
+}
+
+int afx_decode_layer_grid_async(const afx_job *jobs, size_t n_jobs, uint32_t max_workgroups, void *stream) {
+    if (max_workgroups == 0) return AFX_E_INVALID_ARG;
+    const int rc = check_batch(jobs, n_jobs);
+    return rc != AFX_OK ? rc : decode_batch(jobs, n_jobs, max_workgroups, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

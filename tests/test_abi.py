@@ -124,6 +124,12 @@ def test_decode_argument_errors_before_any_hip_call(L):
     jobs = afx.make_jobs([(info, fake_dev, fake_dev * 8, 2 * n), (info, fake_dev, fake_dev * 12, 2 * n),
                           (info, fake_dev * 12, fake_dev * 16, 2 * n)])
     assert L.afx_decode_layer_async(jobs, 3, None) == afx.AFX_E_INVALID_ARG  # job 2's blob is job 1's output
+    # the grid-capped batch: a zero cap, then the same checks as the batch call
+    assert L.afx_decode_layer_grid_async(None, 0, 0, None) == afx.AFX_E_INVALID_ARG
+    assert L.afx_decode_layer_grid_async(None, 0, 1, None) == afx.AFX_OK
+    assert L.afx_decode_layer_grid_async(jobs, 3, 8, None) == afx.AFX_E_INVALID_ARG
+    jobs = afx.make_jobs([(info, fake_dev, fake_dev * 4, 2 * n), (info, fake_dev, fake_dev * 8 + 2, 2 * n)])
+    assert L.afx_decode_layer_grid_async(jobs, 2, 64, None) == afx.AFX_E_MISALIGNED
 
 
 

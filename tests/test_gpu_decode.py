@@ -249,16 +249,22 @@ def test_many_small_tensors_split_over_launches():
         assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
 
 
-def restore_batch_exact(xs, name):
-    """Encode xs with the library, restore them with one batch call into
+def restore_batch_exact(xs, name, max_workgroups=None, blobs=None):
+    """Encode xs with the library (unless blobs are given), restore them with
+    one batch call (on at most max_workgroups workgroups, if given) into
     outputs followed by guard words, and compare every output exactly."""
-    blobs = [afx.afx_encode(x, threads=8) for x in xs]
+    if blobs is None:
+        blobs = [afx.afx_encode(x, threads=8) for x in xs]
     infos = [afx.afx_query(b) for b in blobs]
     devs = [afx.to_device(b) for b in blobs]
     outs = [torch.full((x.size + 64,), 0x5A5A, dtype=torch.int16, device="cuda") for x in xs]
-    say(f"[gpu] case {name}: {len(xs)} tensors, chunks {[int(i.n_chunks) for i in infos]}")
-    afx.afx_decode_layer_async([(i, d.data_ptr(), o.data_ptr(), 2 * x.size)
-                                for i, d, o, x in zip(infos, devs, outs, xs)], 0)
+    say(f"[gpu] case {name}: {len(xs)} tensors, chunks {[int(i.n_chunks) for i in infos]}, "
+        f"max_workgroups {max_workgroups}")
+    jobs = [(i, d.data_ptr(), o.data_ptr(), 2 * x.size) for i, d, o, x in zip(infos, devs, outs, xs)]
+    if max_workgroups is None:
+        afx.afx_decode_layer_async(jobs, 0)
+    else:
+        afx.afx_decode_layer_grid_async(jobs, max_workgroups, 0)
     torch.cuda.synchronize()
     for k, (x, o) in enumerate(zip(xs, outs)):
         y = o.cpu().numpy().view(np.uint16)
@@ -297,6 +303,35 @@ def test_full_launch_of_mixed_tensors():
            for i in range(24)]
     order = rng.permutation(len(xs))
     restore_batch_exact([xs[i] for i in order], "32 mixed tensors")
+
+
+_GRID_BATCH = {}
+
+
+def grid_batch():
+    """A large heavy-tailed tensor (2,000 chunks), three mid-size ones and
+    four small ones, ragged ends, encoded once for every grid cap."""
+    if not _GRID_BATCH:
+        rng = np.random.default_rng(77)
+        xs = [synth.generate(synth.TensorSpec("big", (2000 * 4096 - 123,), "t4", 1000))]
+        xs += [synth.generate(synth.TensorSpec(f"mid{i}", (c * 4096 + 17 * i,), "normal", 1001 + i))
+               for i, c in enumerate((300, 97, 33))]
+        xs += [synth.generate(synth.TensorSpec(f"small{i}", (int(rng.integers(1, 20000)),), "normal", 1010 + i))
+               for i in range(4)]
+        _GRID_BATCH["xs"] = xs
+        _GRID_BATCH["blobs"] = [afx.afx_encode(x, threads=8) for x in xs]
+    return _GRID_BATCH["xs"], _GRID_BATCH["blobs"]
+
+
+@pytest.mark.parametrize("cap", [1, 2, 3, 7, 9, 31, 100, 255, 257, 10**9])
+def test_grid_caps_bit_exact(cap):
+    """The same batch on at most 1 .. 257 workgroups (and a cap above any
+    device): odd workgroup counts exercise the chunk rotation between a
+    tensor's workgroups (ranks counted XCD by XCD), the waves' claiming of
+    long per-workgroup lists, and workgroups that serve several tensors
+    (fewer workgroups than tensors). Every output exact, guards intact."""
+    xs, blobs = grid_batch()
+    restore_batch_exact(xs, f"grid cap {cap}", max_workgroups=cap, blobs=blobs)
 
 
 def test_embedding_full_size():
