@@ -178,9 +178,10 @@ struct GemmLds {
 // partial sums meet in LDS at the end of the tile), so that no wave
 // multiplies alone while the others wait at the barrier. A workgroup thus multiplies each restored slab with
 // 32 kB (4 / kWays) tokens: 32 (kWays 4), 64 (2), 128 (1) or 256 (kB 2).
-// With kB = 2, only the A operands of the slab's first 4 steps are fetched
-// before the restore; each later step's are fetched 4 steps ahead, during
-// the matrix instructions, to fit the registers.
+// With kB = 2, only the A operands of the slab's first 6 steps are fetched
+// before the restore; each later step's are fetched 6 steps ahead, during
+// the matrix instructions (250 registers, two waves per SIMD: 4 steps ahead
+// left more of the loads' latency exposed, 8 spill).
 template <int kB, int kWays>
 __global__ __launch_bounds__(kGemmThreads, kB == 1 ? 3 : 2)
 void afx_gemm_kernel(const GemmBatch batch) {
@@ -250,7 +251,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t ks0 = kSteps * (wave % kWays);
     // A steps fetched before the restore (the rest a few steps ahead during
     // the matrix instructions, where the registers are short)
-    constexpr uint32_t kPre = kB == 2 || kWays == 1 ? kSteps / 4 : kWays == 2 ? kSteps / 2 : kSteps;
+    constexpr uint32_t kPre = kB == 2 ? 6 : kWays == 1 ? kSteps / 4 : kWays == 2 ? kSteps / 2 : kSteps;
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
