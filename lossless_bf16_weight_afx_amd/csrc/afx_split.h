@@ -40,10 +40,10 @@ inline uint64_t split_max_load(const uint64_t *chunks, uint32_t n, uint32_t grid
 // enough workgroups for ceil(total / max_blocks) chunks each; a tensor whose
 // share rounds to nothing takes the one workgroup at its position (with its
 // neighbour). Second candidate, when every large tensor can have workgroups
-// of its own and the small ones one more: each workgroup in turn goes to the
-// large tensor whose busiest workgroup holds the most chunks (which
-// minimises that maximum), then each tensor keeps the fewest workgroups that
-// reach the same maximum, and the small tensors share a last workgroup. The
+// of its own and the small ones one more: the smallest maximum L of chunks
+// per workgroup that the large tensors can reach with disjoint workgroups,
+// each tensor taking the fewest (ceil(c / L)) that reach it, found by
+// bisection; the small tensors share a last workgroup. The
 // second is used only when its busiest workgroup holds strictly fewer
 // chunks: proportional ranges keep each array's workgroups spread over the
 // grid in order, and when the rounding of the shares is harmless (a full
@@ -66,35 +66,38 @@ inline uint32_t split_grid(const uint64_t *chunks, uint32_t n, uint32_t n_big, u
         first += chunks[t];
     }
     const uint32_t extra = n_big < n ? 1u : 0u;
-    if (n_big == 0 || n > 64 || (uint64_t)n_big + extra > max_blocks || grid > kSplitMaxGrid) return grid;
+    if (n_big == 0 || (uint64_t)n_big + extra > max_blocks || grid > kSplitMaxGrid) return grid;
     const uint64_t prop_max = split_max_load(chunks, n, grid, lo, hi);
 
-    uint32_t nb[64];
+    // The fewest chunks L on any large tensor's workgroup such that giving
+    // each tensor ceil(c / L) workgroups stays within the budget (the count
+    // falls as L grows; at the largest c it is one workgroup per tensor).
     uint64_t budget = (uint64_t)max_blocks - extra;
     if (budget > kSplitMaxGrid) budget = kSplitMaxGrid;
-    uint64_t used = n_big;
-    for (uint32_t t = 0; t < n_big; ++t) nb[t] = 1;
-    auto busiest = [&](uint32_t t) { return (chunks[t] + nb[t] - 1) / nb[t]; };
-    while (used < budget) {
-        uint32_t w = 0;
-        for (uint32_t t = 1; t < n_big; ++t)
-            if (busiest(t) > busiest(w)) w = t;
-        if (busiest(w) <= 1) break;
-        ++nb[w];
-        ++used;
+    auto need = [&](uint64_t L) {
+        uint64_t k = 0;
+        for (uint32_t t = 0; t < n_big; ++t) k += (chunks[t] + L - 1) / L;
+        return k;
+    };
+    uint64_t L_lo = 1, L = 1;
+    for (uint32_t t = 0; t < n_big; ++t) L = chunks[t] > L ? chunks[t] : L;
+    while (L_lo < L) {
+        const uint64_t mid = L_lo + (L - L_lo) / 2;
+        if (need(mid) <= budget)
+            L = mid;
+        else
+            L_lo = mid + 1;
     }
-    uint64_t L = 0;
-    for (uint32_t t = 0; t < n_big; ++t) L = busiest(t) > L ? busiest(t) : L;
     uint64_t small_sum = 0;
     for (uint32_t t = n_big; t < n; ++t) small_sum += chunks[t];
     const uint64_t min_max = L > small_sum ? L : small_sum;
     if (min_max >= prop_max) return grid;
     uint32_t at = 0;
     for (uint32_t t = 0; t < n_big; ++t) {
-        nb[t] = (uint32_t)((chunks[t] + L - 1) / L);
+        const uint32_t nb = (uint32_t)((chunks[t] + L - 1) / L);
         lo[t] = at;
-        hi[t] = at + nb[t];
-        at += nb[t];
+        hi[t] = at + nb;
+        at += nb;
     }
     for (uint32_t t = n_big; t < n; ++t) {
         lo[t] = at;

@@ -36,8 +36,9 @@ def test_grid_split(tmp_path):
 
 @pytest.mark.parametrize("what,old,new", [
     ("second candidate always taken", "if (min_max >= prop_max) return grid;", "if (false) return grid;"),
-    ("workgroup given to the least busy tensor", "if (busiest(t) > busiest(w)) w = t;",
-     "if (busiest(t) < busiest(w)) w = t;"),
+    ("workgroups counted with floor division", "for (uint32_t t = 0; t < n_big; ++t) k += (chunks[t] + L - 1) / L;",
+     "for (uint32_t t = 0; t < n_big; ++t) k += chunks[t] / L;"),
+    ("bisection stops one short", "            L_lo = mid + 1;", "            L_lo = mid + 2;"),
 ])
 def test_check_catches_a_planted_mistake(tmp_path, what, old, new):
     d = tmp_path / "csrc"
