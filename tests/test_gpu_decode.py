@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+from blob_damage import damage
 from lossless_bf16_weight_afx_amd import afx, synth
 
 pytestmark = pytest.mark.gpu
@@ -132,32 +133,6 @@ def test_misaligned_output_rejected():
     assert torch.all(out == 7).item()
 
 
-def _damage(blob: np.ndarray, what: str, rng) -> np.ndarray:
-    """A copy of blob with one section damaged as a stale or corrupted
-    device copy might be: random bit flips (high bits included) in the chunk
-    bases, random gaps, random code words, random code lengths (0..255), or
-    all of them at once."""
-    s = oracle.sections(blob)["offsets"]
-    n_chunks = -(-int(oracle.sections(blob)["header"]["n"]) // 4096)
-    c = blob.copy()
-
-    def flip(lo, hi, k):
-        idx = rng.integers(lo, hi, k)
-        c[idx] ^= (np.uint8(1) << rng.integers(0, 8, k).astype(np.uint8))
-
-    if what in ("bases", "all"):
-        flip(s["chunk_base"], s["chunk_base"] + 8 * (n_chunks + 1), max(4, n_chunks))
-    if what in ("gaps", "all"):
-        lo, hi = s["gap"], s["signmant"]
-        c[lo:hi] = rng.integers(0, 256, hi - lo, dtype=np.uint8)
-    if what in ("words", "all"):
-        lo, hi = s["exp"], s["blob_bytes"]
-        c[lo:hi] = rng.integers(0, 256, hi - lo, dtype=np.uint8)
-    if what in ("lengths", "all"):
-        c[s["code_len"]:s["code_len"] + 256] = rng.integers(0, 256, 256, dtype=np.uint8)
-    return c
-
-
 @pytest.mark.parametrize("what", ["bases", "gaps", "words", "lengths", "all"])
 def test_corrupt_device_blob_stays_in_bounds(what):
     """A device blob that differs from the host copy afx_query validated
@@ -174,7 +149,7 @@ def test_corrupt_device_blob_stays_in_bounds(what):
     for x in xs:
         blob = oracle.encode(x)
         info = afx.afx_query(blob)  # the undamaged host copy
-        bad = _damage(blob, what, rng)
+        bad = damage(blob, what, rng)
         dev = afx.to_device(bad)
         n = x.size
         out = torch.full((n + 2 * guard,), 0x5A5A, dtype=torch.int16, device="cuda")
