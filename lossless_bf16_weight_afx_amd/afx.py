@@ -212,6 +212,8 @@ def afx_decode_layer_async(jobs, stream: int = 0) -> None:
 
 def afx_decode_layer_grid_async(jobs, max_workgroups: int, stream: int = 0) -> None:
     """afx_decode_layer_async on at most ``max_workgroups`` workgroups (CUs)."""
+    if not 0 <= int(max_workgroups) < 2 ** 32:
+        raise ValueError(f"max_workgroups {max_workgroups} is not a 32-bit unsigned count")
     arr = jobs if isinstance(jobs, ctypes.Array) else make_jobs(jobs)
     _check(lib().afx_decode_layer_grid_async(arr, len(arr), ctypes.c_uint32(max_workgroups), ctypes.c_void_p(stream)),
            "afx_decode_layer_grid_async")

@@ -130,6 +130,11 @@ def test_decode_argument_errors_before_any_hip_call(L):
     assert L.afx_decode_layer_grid_async(jobs, 3, 8, None) == afx.AFX_E_INVALID_ARG
     jobs = afx.make_jobs([(info, fake_dev, fake_dev * 4, 2 * n), (info, fake_dev, fake_dev * 8 + 2, 2 * n)])
     assert L.afx_decode_layer_grid_async(jobs, 2, 64, None) == afx.AFX_E_MISALIGNED
+    with pytest.raises(ValueError):  # the binding refuses a cap that is no 32-bit count
+        afx.afx_decode_layer_grid_async(jobs, -1)
+    with pytest.raises(afx.AfxError) as e:
+        afx.afx_decode_layer_grid_async(jobs, 0)
+    assert e.value.status == afx.AFX_E_INVALID_ARG
 
 
 
