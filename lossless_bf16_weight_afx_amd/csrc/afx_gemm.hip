@@ -181,7 +181,9 @@ struct GemmLds {
 // With kB = 2, only the A operands of the slab's first 6 steps are fetched
 // before the restore; each later step's are fetched 6 steps ahead, during
 // the matrix instructions (250 registers, two waves per SIMD: 4 steps ahead
-// left more of the loads' latency exposed, 8 spill).
+// left more of the loads' latency exposed, 8 spill). With 128 tokens per
+// workgroup (kB = 1, kWays = 1) the lead is 5 of 16 steps, the most that
+// keeps three workgroups per CU without spills.
 template <int kB, int kWays>
 __global__ __launch_bounds__(kGemmThreads, kB == 1 ? 3 : 2)
 void afx_gemm_kernel(const GemmBatch batch) {
@@ -251,7 +253,7 @@ void afx_gemm_kernel(const GemmBatch batch) {
     const uint32_t ks0 = kSteps * (wave % kWays);
     // A steps fetched before the restore (the rest a few steps ahead during
     // the matrix instructions, where the registers are short)
-    constexpr uint32_t kPre = kB == 2 ? 6 : kWays == 1 ? kSteps / 4 : kWays == 2 ? kSteps / 2 : kSteps;
+    constexpr uint32_t kPre = kB == 2 ? 6 : kWays == 1 ? 5 : kWays == 2 ? kSteps / 2 : kSteps;
     for (uint32_t k0 = kbeg; k0 < kend; k0 += kSlabCols) {
         const bool has_n = k0 + kSlabCols < kend, has_nn = k0 + 2 * kSlabCols < kend;
         // Stage this slab's code words (loaded a slab ago; a segment longer
