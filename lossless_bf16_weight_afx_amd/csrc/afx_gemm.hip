@@ -11,10 +11,11 @@
 // and Y is FP32 [m, rows], both row-major: Y[t, r] += sum_k X[t, k] W[r, k].
 //
 // Work decomposition:
-//   * a tile is 64 rows of W by a range of up to 2560 columns; a workgroup of
-//     4 wave64s takes one tile and up to 128 tokens (blockIdx.y picks the
-//     token block). Every tile adds its partial sums into Y with atomic adds,
-//     so ranges of one row may run on different workgroups;
+//   * a tile is 64 rows of W by a range of up to 2560 columns (5120 when a
+//     workgroup takes 256 tokens); a workgroup of 4 wave64s takes one tile
+//     and up to 256 tokens (the block index picks the token block). Every
+//     tile adds its partial sums into Y with atomic adds, so ranges of one
+//     row may run on different workgroups;
 //   * the tile's columns are restored 256 at a time (a slab of 64 x 256
 //     values). A 32-element group decodes on its own from its chunk's bit
 //     base and its gap, so a slab is 64 x 8 groups: wave w restores rows
@@ -42,8 +43,11 @@ constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = kGemmWaves * kWave;             // 256
 constexpr uint32_t kTileRows = 64;                           // W rows per tile (two MFMA N blocks)
 constexpr uint32_t kSlabCols = 256;                          // columns restored per step
-constexpr uint32_t kRangeSlabs = 10;                         // a tile spans <= 2560 columns
-constexpr uint32_t kRangeCols = kRangeSlabs * kSlabCols;
+constexpr uint32_t kRangeSlabs = 10;                         // slabs per tile per 32-token block of a wave
+// Columns of a tile: 2560 with one 32-token block per wave, 5120 with two
+// (their slabs take longer to multiply, so fewer tiles balance the grid).
+template <int kB>
+constexpr uint32_t range_cols() { return kRangeSlabs * kB * kSlabCols; }
 constexpr uint32_t kMaxTokenBlocks = 2;                      // 32-token blocks per wave (1 or 2)
 constexpr uint32_t kRowsPerWave = kTileRows / kGemmWaves;    // 16
 // A row segment's code words (kSegWords, staged in reverse in a slice of
@@ -65,6 +69,8 @@ struct GemmBatch {
     GemmJob j[AFX_MAX_GEMV_JOBS_PER_LAUNCH];
     uint32_t n;
     uint32_t m;
+    uint32_t tiles;  // tiles of all jobs
+    uint32_t n_tok;  // token blocks (workgroups per tile)
 };
 
 // 16 bytes of x as the A operand (zeros for a token beyond m).
@@ -194,17 +200,26 @@ void afx_gemm_kernel(const GemmBatch batch) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // Block b runs on XCD b mod 8. Each run of 8 n_tok blocks takes 8 tiles
+    // (one per XCD) times the n_tok token blocks, so that the workgroups that
+    // restore one tile for different tokens run on the same XCD close in
+    // time and find its compressed bytes in that XCD's L2. With one token
+    // block this is block b = tile b.
+    const uint32_t nt = batch.n_tok;
+    const uint32_t gtile = (blockIdx.x / (8 * nt)) * 8 + blockIdx.x % 8, tblk = (blockIdx.x / 8) % nt;
+    if (gtile >= batch.tiles) return;  // the last run's padding
     uint32_t jb = 0;
     for (uint32_t i = 1; i < batch.n; ++i)
-        if (blockIdx.x >= batch.j[i].tile0) jb = i;
+        if (gtile >= batch.j[i].tile0) jb = i;
     const GemmJob &J = batch.j[jb];
     const TensorDesc &T = J.t;
-    const uint32_t tile = blockIdx.x - J.tile0;
+    const uint32_t tile = gtile - J.tile0;
     const uint32_t r0 = (tile % J.n_rtiles) * kTileRows;
+    constexpr uint32_t kRangeCols = range_cols<kB>();
     const uint32_t kbeg = (tile / J.n_rtiles) * kRangeCols;
     const uint32_t kend = min(J.cols, kbeg + kRangeCols);
     static_assert(kGemmWaves % kWays == 0 && (kSlabCols / 16) % kWays == 0, "waves share a token block's steps");
-    const uint32_t t0 = blockIdx.y * (32 * kB * (kGemmWaves / kWays));
+    const uint32_t t0 = tblk * (32 * kB * (kGemmWaves / kWays));
     const uint32_t m = batch.m;
 
     // The code lengths and the first slabs' bit offsets are requested
@@ -404,10 +419,11 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     GemmBatch batch{};
     batch.m = m;
     uint64_t tiles = 0;
+    const uint32_t rc = m > kGemmWaves * 32 ? range_cols<2>() : range_cols<1>();  // as the kernel launched below
     for (size_t i = 0; i < n_jobs; ++i) {
         GemmJob g = gemm_job(jobs[i]);
         g.tile0 = (uint32_t)tiles;
-        tiles += (uint64_t)g.n_rtiles * ((g.cols + kRangeCols - 1) / kRangeCols);
+        tiles += (uint64_t)g.n_rtiles * ((g.cols + rc - 1) / rc);
         batch.j[batch.n++] = g;
     }
     if (tiles == 0) return AFX_OK;
@@ -417,12 +433,17 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     // 128 tokens cover m, else two per wave
     const uint32_t per_wg = m <= 32 ? 32 : m <= 64 ? 64 : m <= kGemmWaves * 32 ? kGemmWaves * 32 : kGemmWaves * 64;
     const uint32_t tok_blocks = (m + per_wg - 1) / per_wg;
+    // with several token blocks, the tiles padded to a multiple of 8 (see the kernel)
+    const uint64_t blocks = tok_blocks == 1 ? tiles : (tiles + 7) / 8 * 8 * tok_blocks;
+    if (blocks >= (1ull << 31)) return AFX_E_UNSUPPORTED;
+    batch.tiles = (uint32_t)tiles;
+    batch.n_tok = tok_blocks;
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
     const void *fn = m <= 32   ? reinterpret_cast<const void *>(&afx_gemm_kernel<1, 4>)
                      : m <= 64 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1, 2>)
                      : m <= kGemmWaves * 32 ? reinterpret_cast<const void *>(&afx_gemm_kernel<1, 1>)
                                             : reinterpret_cast<const void *>(&afx_gemm_kernel<2, 1>);
-    return hipLaunchKernel(fn, dim3((unsigned)tiles, tok_blocks), dim3(kGemmThreads), args, 0, stream) == hipSuccess
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kGemmThreads), args, 0, stream) == hipSuccess
                ? AFX_OK
                : AFX_E_HIP;
 }

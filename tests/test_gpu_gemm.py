@@ -61,6 +61,8 @@ def small_ints(rng, shape, lo, hi):
     (128, 2816, 48),    # two waves share each token block (partial second block), two column ranges
     (64, 1024, 100),    # one block per wave, the fourth partial
     (64, 768, 20),      # four waves share one partial token block
+    (64, 17408, 300),   # two token blocks per wave over 5120-column ranges (3 + a 2048 remainder)
+    (128, 5376, 200),   # two token blocks per wave, a 5120-column range and a 256-column one
 ])
 def test_integer_data_exact(rows, cols, m):
     say(f"[gpu] case gemm integers {rows}x{cols} m={m}")
