@@ -200,13 +200,10 @@ void afx_gemm_kernel(const GemmBatch batch) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    // Block b runs on XCD b mod 8. Each run of 8 n_tok blocks takes 8 tiles
-    // (one per XCD) times the n_tok token blocks, so that the workgroups that
-    // restore one tile for different tokens run on the same XCD close in
-    // time and find its compressed bytes in that XCD's L2. With one token
-    // block this is block b = tile b.
-    const uint32_t nt = batch.n_tok;
-    const uint32_t gtile = (blockIdx.x / (8 * nt)) * 8 + blockIdx.x % 8, tblk = (blockIdx.x / 8) % nt;
+    // The launch order (afx_index.h): the workgroups that restore one tile
+    // for different tokens run on the same XCD close in time and find its
+    // compressed bytes in that XCD's L2.
+    const uint32_t gtile = gemm_block_tile(blockIdx.x, batch.n_tok), tblk = gemm_block_token(blockIdx.x, batch.n_tok);
     if (gtile >= batch.tiles) return;  // the last run's padding
     uint32_t jb = 0;
     for (uint32_t i = 1; i < batch.n; ++i)
@@ -434,7 +431,7 @@ int launch_gemm(const afx_gemv_job *jobs, size_t n_jobs, uint32_t m, hipStream_t
     const uint32_t per_wg = m <= 32 ? 32 : m <= 64 ? 64 : m <= kGemmWaves * 32 ? kGemmWaves * 32 : kGemmWaves * 64;
     const uint32_t tok_blocks = (m + per_wg - 1) / per_wg;
     // with several token blocks, the tiles padded to a multiple of 8 (see the kernel)
-    const uint64_t blocks = tok_blocks == 1 ? tiles : (tiles + 7) / 8 * 8 * tok_blocks;
+    const uint64_t blocks = gemm_blocks(tiles, tok_blocks);
     if (blocks >= (1ull << 31)) return AFX_E_UNSUPPORTED;
     batch.tiles = (uint32_t)tiles;
     batch.n_tok = tok_blocks;

@@ -152,4 +152,16 @@ constexpr uint32_t seg_chain_r0(uint64_t p, uint64_t wa) {
     return 32 * kSegRev - (uint32_t)umin64(p - 32 * wa, kSegMaxStart);
 }
 
+// ---- the MFMA product's launch order ----------------------------------------
+// Not derived from blob contents, but checked with the rest: block b of a
+// launch with nt token blocks per tile takes tile gemm_block_tile(b, nt) (at
+// least the tile count for the padding of the last run) and token block
+// gemm_block_token(b, nt). Block b runs on XCD b mod 8, and each run of 8 nt
+// blocks covers 8 tiles (one per XCD) times the nt token blocks, so the
+// workgroups that restore one tile for different tokens run on one XCD close
+// together. With nt = 1 block b takes tile b.
+constexpr uint32_t gemm_block_tile(uint32_t b, uint32_t nt) { return (b / (8 * nt)) * 8 + b % 8; }
+constexpr uint32_t gemm_block_token(uint32_t b, uint32_t nt) { return (b / 8) % nt; }
+constexpr uint64_t gemm_blocks(uint64_t tiles, uint32_t nt) { return nt == 1 ? tiles : (tiles + 7) / 8 * 8 * nt; }
+
 }  // namespace afx

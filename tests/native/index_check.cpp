@@ -8,11 +8,13 @@
 // compose them, with random bit positions, gaps, code lengths, step sizes
 // and section sizes, many of them wild (end before start, values near
 // 2^64), and checks every LDS slot and global word index against the buffer
-// it addresses. Built with AddressSanitizer and UndefinedBehaviorSanitizer by
+// it addresses; and that the MFMA product's launch order gives every tile
+// and token block to exactly one workgroup. Built with AddressSanitizer and UndefinedBehaviorSanitizer by
 // tests/test_index_bounds.py; exits 1 on the first few violations it prints.
 #include <cstdint>
 #include <cstdio>
 #include <random>
+#include <vector>
 
 #include "afx_index.h"
 
@@ -160,6 +162,26 @@ void gemm_segment(Rng &R, uint64_t exp_words) {
     }
 }
 
+// The MFMA product's launch order: every (tile, token block) pair taken by
+// exactly one block, padding blocks only past the last tile.
+void gemm_order(Rng &R) {
+    const uint64_t tiles = 1 + R.below(R.below(2) ? 40 : 3000);
+    const uint32_t nt = 1 + R.below(R.below(2) ? 3 : 9);
+    const uint64_t blocks = gemm_blocks(tiles, nt);
+    CHECK(blocks >= tiles * nt && blocks < tiles * nt + 8 * nt, "launch of %llu blocks", (unsigned long long)blocks);
+    std::vector<uint8_t> seen(tiles * nt, 0);
+    for (uint64_t b = 0; b < blocks; ++b) {
+        const uint32_t t = gemm_block_tile((uint32_t)b, nt), k = gemm_block_token((uint32_t)b, nt);
+        CHECK(k < nt, "token block %u of %u", k, nt);
+        if (t >= tiles || k >= nt) continue;
+        CHECK(t % 8 == b % 8 || nt == 1, "tile %u off its block's XCD", t);
+        CHECK(!seen[t * nt + k], "tile %u token block %u taken twice", t, k);
+        seen[t * nt + k] = 1;
+    }
+    for (uint64_t i = 0; i < tiles * nt; ++i) CHECK(seen[i], "tile %llu token block %llu not taken",
+                                                    (unsigned long long)(i / nt), (unsigned long long)(i % nt));
+}
+
 }  // namespace
 
 int main(int argc, char **argv) {
@@ -175,6 +197,7 @@ int main(int argc, char **argv) {
         restore_chunk(R, n, exp_words);
         table_reads(R);
         gemm_segment(R, exp_words);
+        if (t % 64 == 0) gemm_order(R);
     }
     std::printf("%llu index checks, %llu out of range\n", (unsigned long long)g_checks, (unsigned long long)g_fail);
     return g_fail ? 1 : 0;

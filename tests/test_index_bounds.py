@@ -46,6 +46,8 @@ def test_every_index_in_range(tmp_path):
      "constexpr uint32_t gap_slot(uint32_t g, uint32_t ng) { return g; }"),
     ("segment chain start unclamped", "return 32 * kSegRev - (uint32_t)umin64(p - 32 * wa, kSegMaxStart);",
      "return 32 * kSegRev - (uint32_t)(p - 32 * wa);"),
+    ("launch order's token block off by a factor", "constexpr uint32_t gemm_block_token(uint32_t b, uint32_t nt) { return (b / 8) % nt; }",
+     "constexpr uint32_t gemm_block_token(uint32_t b, uint32_t nt) { return b % nt; }"),
 ])
 def test_check_catches_a_removed_clamp(tmp_path, what, old, new):
     """Control: the check is able to fail (each clamp it relies on matters)."""
