@@ -330,7 +330,7 @@ def main() -> int:
 def copy_ceiling(stream, traffic: int, copies: int):
     """A plain elementwise copy kernel (torch's bitwise_not over int16: read
     N, write N bytes) moving `traffic` bytes per launch over `copies`
-    rotated regions: the box's practical ceiling for that traffic, and the
+    rotated regions: the GPU's practical ceiling for that traffic, and the
     known-size kernel that calibrates rocprofv3's HBM byte counters.
     Returns (GB/s, N)."""
     import torch

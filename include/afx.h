@@ -60,7 +60,7 @@ typedef enum afx_status {
     AFX_E_BUFFER_TOO_SMALL = -5,/* blob shorter than its header says, or output too small */
     AFX_E_MISALIGNED = -6,      /* device pointer not 16-byte aligned */
     AFX_E_HIP = -7,             /* a HIP runtime call failed (launch or execution) */
-    AFX_E_UNSUPPORTED = -8,     /* request beyond what this build supports */
+    AFX_E_UNSUPPORTED = -8,     /* request beyond what the library supports */
     AFX_E_IO = -9,              /* a file could not be opened or read in full */
     AFX_E_HOST_MEMORY = -10     /* host memory for the call's own work could not be had */
 } afx_status;

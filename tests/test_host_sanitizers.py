@@ -4,7 +4,7 @@ UndefinedBehaviorSanitizer (CPU only).
 tests/native/host_check.cpp drives the encoder, blob validation, the host
 unpack, the file reader and the oracle's encoder and decoders, including on
 damaged blobs; here it is built with g++/gcc with both sanitizers (host code
-only: no HIP source is part of this build) and must finish cleanly.
+only: no HIP source is part of that program) and must finish cleanly.
 """
 import os
 import subprocess
