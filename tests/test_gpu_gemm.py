@@ -76,6 +76,24 @@ def test_integer_data_exact(rows, cols, m):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("m", [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513])
+def test_token_counts_at_every_variant_boundary(m):
+    """Exact at the token counts where the kernel variant (four, two or one
+    waves per 32-token block, two blocks per wave) or the number of 256-token
+    blocks per tile changes; 513 tokens make three blocks per tile, dispatched
+    together on one XCD."""
+    say(f"[gpu] case gemm integers 128x1024 m={m}")
+    rng = np.random.default_rng(5000 + m)
+    rows, cols = 128, 1024
+    w = small_ints(rng, rows * cols, -3, 3)
+    x = small_ints(rng, (m, cols), -2, 2)
+    blob = oracle.encode(w, (rows, cols))
+    got = gemm(blob, rows, cols, x, m)
+    ref, _ = oracle.restore_gemv(blob, rows, cols, x, threads=4)
+    assert np.abs(ref).max() < 2 ** 24
+    assert np.array_equal(got, ref)
+
+
 def check(blob, rows, cols, x, m, y0=None):
     got = gemm(blob, rows, cols, x, m, y0)
     ref, bound = oracle.restore_gemv(blob, rows, cols, x, threads=4,
