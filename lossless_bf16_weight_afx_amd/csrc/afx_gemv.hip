@@ -28,6 +28,7 @@
 #include <atomic>
 
 #include "afx_device.h"
+#include "afx_split.h"
 
 namespace afx {
 namespace {
@@ -394,27 +395,22 @@ int gemv_max_blocks(int *out) {
     return AFX_OK;
 }
 
-// One launch for up to kMaxGemvJobs checked matrices: the grid is split
-// among them in proportion to their chunk counts, as for a restore batch.
+// One launch for up to kMaxGemvJobs checked matrices (each of at least one
+// chunk): the grid is split among them by their chunk counts with the
+// restore's split (afx_split.h), every matrix counted as large.
 template <int M, bool kLong>
 int launch_gemv_kernel(GemvBatch &batch, hipStream_t stream) {
-    uint64_t total = 0, first[kMaxGemvJobs];
-    for (uint32_t t = 0; t < batch.n; ++t) {
-        first[t] = total;
-        total += batch.j[t].t.n_chunks;
-    }
-    if (total == 0) return AFX_OK;
+    uint64_t chunks[kMaxGemvJobs];
+    uint32_t lo[kMaxGemvJobs], hi[kMaxGemvJobs];
+    for (uint32_t t = 0; t < batch.n; ++t) chunks[t] = batch.j[t].t.n_chunks;
+    if (batch.n == 0) return AFX_OK;
     int max_blocks = 0;
     const int rc = gemv_max_blocks<M, kLong>(&max_blocks);
     if (rc != AFX_OK) return rc;
-    const uint64_t per_block = (total + max_blocks - 1) / max_blocks;
-    const uint64_t grid = std::max<uint64_t>(1, (total + per_block - 1) / per_block);
+    const uint32_t grid = split_grid(chunks, batch.n, batch.n, (uint32_t)max_blocks, lo, hi);
     for (uint32_t t = 0; t < batch.n; ++t) {
-        const uint64_t lo = grid * first[t] / total;
-        uint64_t hi = grid * (first[t] + batch.j[t].t.n_chunks) / total;
-        if (hi <= lo) hi = lo + 1;
-        batch.j[t].t.blk_lo = (uint32_t)lo;
-        batch.j[t].t.blk_hi = (uint32_t)hi;
+        batch.j[t].t.blk_lo = lo[t];
+        batch.j[t].t.blk_hi = hi[t];
     }
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
     return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemv_kernel<M, kLong>), dim3((unsigned)grid),
