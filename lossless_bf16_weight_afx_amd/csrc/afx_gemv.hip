@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <numeric>
 
 #include "afx_device.h"
 #include "afx_split.h"
@@ -39,10 +40,20 @@ struct GemvArgs {
     float *y;           // [m, rows] FP32, accumulated into
     uint64_t rows;
     uint32_t cols;      // a multiple of 8 (every 8 consecutive values lie in one row), below 2^31
-    uint32_t reserved;
+    // 0, or P when x is staged as a window of one chunk's columns per token:
+    // the columns of chunk c start at (c kChunk) mod cols, which repeats with
+    // period P = cols / gcd(cols, kChunk) in c, and every workgroup of this
+    // matrix serves chunks of one residue mod P (its count is a multiple of P)
+    uint32_t xwin;
 };
 
 constexpr uint32_t kMaxGemvJobs = AFX_MAX_GEMV_JOBS_PER_LAUNCH;
+
+// Whether the kernel for M tokens can stage x as a window of one chunk's
+// columns (for one token, x of rows up to 20,480 columns fits whole; the
+// window path stays out of that kernel, whose instruction count is its bound).
+template <int M>
+constexpr bool kWindowed = M >= 2;
 
 struct GemvBatch {
     GemvArgs j[kMaxGemvJobs];
@@ -95,11 +106,12 @@ __device__ inline void load_signmant(const TensorDesc &T, uint64_t lc, int lane,
 // pointer, which waits on both memory counters.
 template <int M>
 __device__ inline void load_x(const GemvArgs &a, const uint16_t *xs, bool x_in_lds,
-                              const __amdgpu_buffer_rsrc_t (&xrow)[M], uint32_t col, uint4 (&xv)[M]) {
+                              const __amdgpu_buffer_rsrc_t (&xrow)[M], uint32_t col, uint4 (&xv)[M],
+                              uint32_t xs_stride, uint32_t xs_col) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         if (x_in_lds) {
-            xv[m] = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * a.cols + col);
+            xv[m] = *reinterpret_cast<const uint4 *>(xs + (uint32_t)m * xs_stride + xs_col);
         } else {
             const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xrow[m], 2 * col, 0, 0);
             xv[m] = make_uint4(t.x, t.y, t.z, t.w);
@@ -143,7 +155,7 @@ __device__ inline void round_products(const GemvArgs &a, const uint4 (&xv)[M], u
 // rounds lie in one row until its columns wrap, then in the next; the
 // products go into a0 (first row) or a1 (second), per token. x is requested
 // kBatch rounds at a time.
-template <int M, int kBatch>
+template <int M, int kBatch, bool kWin>
 __device__ inline void long_rounds(const GemvArgs &a, const uint16_t *xs, bool x_in_lds,
                                    const __amdgpu_buffer_rsrc_t (&xrow)[M], const uint2 (&smv)[8],
                                    const uint8_t *exb, const uint8_t *sm, uint32_t ne, uint32_t c0, int lane,
@@ -155,10 +167,12 @@ __device__ inline void long_rounds(const GemvArgs &a, const uint16_t *xs, bool x
         bool next_row[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-            const uint32_t c = c0 + (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
+            const uint32_t i = (uint32_t)(r0 + q) * (8 * kWave) + 8 * (uint32_t)lane;
+            const uint32_t c = c0 + i;
             next_row[q] = c >= a.cols;
             col[q] = next_row[q] ? c - a.cols : c;
-            load_x<M>(a, xs, x_in_lds, xrow, col[q], xv[q]);
+            // a window holds the chunk's columns in chunk order
+            load_x<M>(a, xs, x_in_lds, xrow, col[q], xv[q], kWin ? kChunk : a.cols, kWin ? i : col[q]);
         }
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
@@ -181,7 +195,7 @@ __device__ inline void long_rounds(const GemvArgs &a, const uint16_t *xs, bool x
 // have been used, the bytes of chunk next_lc (if any) are requested into it,
 // so that their latency overlaps the rest of this chunk and the next decode.
 template <int M, bool kLong>
-__device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_in_lds, uint64_t lc, uint2 (&smv)[8],
+__device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_in_lds, bool x_win, uint64_t lc, uint2 (&smv)[8],
                                   bool has_next, uint64_t next_lc, const ChunkGeom &g, const Gaps &gaps,
                                   const uint32_t *plut, uint32_t *stage, int lane, uint64_t later_bases,
                                   ChunkGeom &later) {
@@ -214,10 +228,12 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
         // so that the reads wait once per batch rather than once per round.
         // x staged in LDS: one round at a time (batched, the LDS reads
         // conflicted more).
-        if (x_in_lds)
-            long_rounds<M, 1>(a, xs, true, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
+        if (kWindowed<M> && x_win)
+            long_rounds<M, 1, true>(a, xs, true, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
+        else if (x_in_lds)
+            long_rounds<M, 1, false>(a, xs, true, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
         else
-            long_rounds<M, (M >= 4 ? 1 : 4 / M)>(a, xs, false, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
+            long_rounds<M, (M >= 4 ? 1 : 4 / M), false>(a, xs, false, xrow, smv, exb, sm, ne, c0, lane, a0, a1);
         if (has_next) load_signmant(T, next_lc, lane, smv);
         // Sum each row's products over the wave and add them into y.
 #pragma unroll
@@ -248,7 +264,7 @@ __device__ inline void gemv_chunk(const GemvArgs &a, const uint16_t *xs, bool x_
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
         uint4 xv[M];
-        load_x<M>(a, xs, x_in_lds, xrow, col, xv);
+        load_x<M>(a, xs, x_in_lds, xrow, col, xv, a.cols, col);
         round_products<M>(a, xv, smv[r], exb, sm, i, ne, col, acc[r]);
     }
     if (has_next) load_signmant(T, next_lc, lane, smv);
@@ -330,10 +346,21 @@ void afx_gemv_kernel(const GemvBatch batch) {
         if (threadIdx.x == 0) next_j = 2 * kWavesPerBlock;
         // stage the activations (read by every chunk) when they fit
         const uint64_t xbytes = (uint64_t)M * a.cols * 2;
-        const bool x_in_lds = xbytes <= kXStageBytes;
-        if (x_in_lds)
+        const bool x_win = kLong && kWindowed<M> && a.xwin != 0;
+        const bool x_in_lds = xbytes <= kXStageBytes || x_win;
+        if (x_win) {
+            // the columns of this workgroup's chunks: (s + j) mod cols, j < kChunk
+            // (s and cols are multiples of 8, so no 8 values straddle the wrap)
+            const uint32_t s = (uint32_t)((uint64_t)(k % a.xwin) * kChunk % a.cols);
+            for (uint32_t i = threadIdx.x; i < M * (kChunk / 8); i += kThreads) {
+                const uint32_t m = i / (kChunk / 8), j = 8 * (i % (kChunk / 8));
+                const uint32_t c = s + j >= a.cols ? s + j - a.cols : s + j;
+                reinterpret_cast<uint4 *>(xs)[i] = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)m * a.cols + c);
+            }
+        } else if (x_in_lds) {
             for (uint32_t i = threadIdx.x; i < xbytes / 16; i += kThreads)
                 reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(a.x)[i];
+        }
         build_lut<kThreads, true>(wave < kSymbolWaves ? len_any : 0u, plut, scratch);
         __syncthreads();  // the pair table is complete
         if (!has_c) continue;
@@ -359,7 +386,7 @@ void afx_gemv_kernel(const GemvBatch batch) {
                 if (has_nn) bases_nn = load_bases(T, k + (uint64_t)jnn * nb, lane);
             }
             ChunkGeom gnn;
-            gemv_chunk<M, kLong>(a, xs, x_in_lds, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, plut, my_stage,
+            gemv_chunk<M, kLong>(a, xs, x_in_lds, x_win, k + (uint64_t)jc * nb, smv, has_n, k + (uint64_t)jn * nb, g, gaps, plut, my_stage,
                           lane, bases_nn, gnn);
             if (!has_n) break;
             wave_sync();  // the exponent bytes have been read
@@ -408,9 +435,24 @@ int launch_gemv_kernel(GemvBatch &batch, hipStream_t stream) {
     const int rc = gemv_max_blocks<M, kLong>(&max_blocks);
     if (rc != AFX_OK) return rc;
     const uint32_t grid = split_grid(chunks, batch.n, batch.n, (uint32_t)max_blocks, lo, hi);
+    const uint64_t busiest = split_max_load(chunks, batch.n, grid, lo, hi);  // 0: not computed
     for (uint32_t t = 0; t < batch.n; ++t) {
-        batch.j[t].t.blk_lo = lo[t];
-        batch.j[t].t.blk_hi = hi[t];
+        GemvArgs &a = batch.j[t];
+        // When x is too large to stage whole but one chunk's columns of it
+        // fit, stage those: every workgroup's chunks then need the same
+        // columns if the matrix's workgroup count is a multiple of their
+        // period, so trim the range to one when that loads no workgroup more
+        // than the busiest of the launch (the trimmed ones skip the matrix).
+        a.xwin = 0;
+        const uint32_t period = a.cols / std::gcd(a.cols, kChunk);
+        const uint32_t nb = hi[t] - lo[t], nbw = nb / period * period;
+        if (kLong && kWindowed<M> && busiest && (uint64_t)M * a.cols * 2 > kXStageBytes && M * kChunk * 2 <= kXStageBytes &&
+            nbw > 0 && (chunks[t] + nbw - 1) / nbw <= busiest) {
+            hi[t] = lo[t] + nbw;
+            a.xwin = period;
+        }
+        a.t.blk_lo = lo[t];
+        a.t.blk_hi = hi[t];
     }
     void *args[] = {&batch};  // hipLaunchKernel reports this launch's own status
     return hipLaunchKernel(reinterpret_cast<const void *>(&afx_gemv_kernel<M, kLong>), dim3((unsigned)grid),
@@ -460,7 +502,7 @@ GemvArgs gemv_args(const afx_gemv_job &j) {
     a.y = j.y_dev;
     a.rows = j.rows;
     a.cols = (uint32_t)j.cols;
-    a.reserved = 0;
+    a.xwin = 0;
     return a;
 }
 

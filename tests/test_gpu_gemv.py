@@ -132,6 +132,38 @@ def test_batch_of_long_rows(m):
         assert np.all(err <= bound), shape
 
 
+@pytest.mark.parametrize("m", [2, 4])
+@pytest.mark.parametrize("rows_a,rows_d", [(64, 192), (128, 384)])
+def test_long_activations_staged_as_a_chunk_window(m, rows_a, rows_d):
+    """Rows of 17,408 columns whose activations (m x 17,408 BF16) do not fit
+    the activation stage: when the matrix's workgroup count is a multiple of
+    17 (the period, in chunks, of a chunk's starting column), each workgroup
+    stages just the 4,096 columns its chunks cover, in chunk order. On a
+    256-CU GPU these batches take that path: D's share of the grid is 204
+    workgroups as split (64, 192), or 234 trimmed to 221 (128, 384). Small
+    integers keep every sum exact, so a wrong column shows."""
+    shapes = [(rows_a, 5120), (rows_d, 17408)]
+    rng = np.random.default_rng(60 + m + rows_a)
+    jobs, keep, refs = [], [], []
+    for rows, cols in shapes:
+        w = synth.f32_to_bf16_bits(rng.integers(-3, 4, size=rows * cols).astype(np.float32))
+        blob = oracle.encode(w, (rows, cols))
+        info = afx.afx_query(blob)
+        db = afx.to_device(blob)
+        x = synth.f32_to_bf16_bits(rng.integers(-2, 3, size=(m, cols)).astype(np.float32))
+        xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+        y = torch.zeros((m, rows), dtype=torch.float32, device="cuda")
+        keep.append((info, db, xd, y))
+        jobs.append((info, db.data_ptr(), rows, cols, xd.data_ptr(), y.data_ptr()))
+        refs.append(oracle.restore_gemv(blob, rows, cols, x, threads=4)[0])
+    say(f"[gpu] case gemv chunk-window activations {shapes}, m={m}")
+    afx.afx_restore_gemv_batch_async(jobs, m, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for (info, db, xd, y), ref, shape in zip(keep, refs, shapes):
+        assert np.abs(ref).max() < 2 ** 24
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), ref), shape
+
+
 def test_graph_replays_within_bound():
     """A fused matrix-vector product captured in a HIP graph (through
     torch.cuda.graph) after a fill kernel that clears y, replayed three
